@@ -1,0 +1,146 @@
+"""Ring KV cache state, write and delta rotation in float64 (test infrastructure).
+
+Runway Characters paper:
+
+* §4.1 "A ring cache with a device-side write position": each new frame goes
+  to a circular slot; a ring is correct only if each cached entry keeps the
+  position it was written with.
+* §4.2 and Appendix G "Cache update and position reset": RoPE is applied to
+  each new key once, before the write; at a reset every cached key is
+  dequantized, rotated by the position change in fp32, and requantized; the
+  values are not touched.
+* §4.3 "FP8 at write": K and V are stored in FP8 and only the new tokens are
+  quantized.
+
+Readings taken where the pages are silent or differ from the hot path's
+statement (each is listed in the design doc):
+
+* scale rule: per-(token, head) s = fp32(margin * amax / 448), margin 1.0,
+  amax over the RoPE'd K vector (float64, no intermediate rounding) and over
+  the raw V vector;
+* the reset recomputes the scale from the rotated key's amax, so the scale
+  rule holds for every cached key after a reset (keeping the old scale with a
+  margin of 1.0 would saturate about half of the keys);
+* the valid set is the cyclic slot range [head - n_valid, head); only valid
+  slots are rotated and their positions shifted.
+
+State layout (canonical, independent of any device layout): codes [H][N][D]
+uint8, scales [H][N] float64 holding fp32 values, slot_pos [N] int64.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import e4m3
+from .rope import delta_angles, rope, rotate_pairs
+
+
+@dataclass
+class RingState:
+    n_slots: int
+    n_heads: int
+    head_dim: int
+    rope_base: float = 10000.0
+    margin: float = 1.0
+    head: int = 0
+    n_valid: int = 0
+    slot_pos: np.ndarray = field(default=None)
+    codes_k: np.ndarray = field(default=None)
+    codes_v: np.ndarray = field(default=None)
+    scale_k: np.ndarray = field(default=None)
+    scale_v: np.ndarray = field(default=None)
+
+    def __post_init__(self):
+        n, h, d = self.n_slots, self.n_heads, self.head_dim
+        if self.slot_pos is None:
+            self.slot_pos = np.zeros(n, dtype=np.int64)
+        if self.codes_k is None:
+            self.codes_k = np.zeros((h, n, d), dtype=np.uint8)
+        if self.codes_v is None:
+            self.codes_v = np.zeros((h, n, d), dtype=np.uint8)
+        if self.scale_k is None:
+            self.scale_k = np.zeros((h, n), dtype=np.float64)
+        if self.scale_v is None:
+            self.scale_v = np.zeros((h, n), dtype=np.float64)
+
+    def copy(self) -> "RingState":
+        return RingState(self.n_slots, self.n_heads, self.head_dim, self.rope_base, self.margin,
+                         self.head, self.n_valid, self.slot_pos.copy(), self.codes_k.copy(),
+                         self.codes_v.copy(), self.scale_k.copy(), self.scale_v.copy())
+
+
+def valid_slots(st: RingState) -> np.ndarray:
+    """Physical slots of the valid range, oldest first: (head - n_valid + k) mod N."""
+    k = np.arange(st.n_valid, dtype=np.int64)
+    return (st.head - st.n_valid + k) % st.n_slots
+
+
+def write_slots(st: RingState, n: int) -> np.ndarray:
+    """Slots the next write of n tokens goes to: (head + i) mod N."""
+    return (st.head + np.arange(n, dtype=np.int64)) % st.n_slots
+
+
+def write(st: RingState, k: np.ndarray, v: np.ndarray, pos: np.ndarray) -> None:
+    """Write n new tokens: RoPE on K at their positions, FP8 quantize K and V.
+
+    k, v: [n, H, D] float64 (bf16 values); pos: [n] integer positions.
+    Token i goes to slot (head + i) mod N and the slot remembers pos[i].
+    Then head <- (head + n) mod N and n_valid <- min(n_valid + n, N).
+    """
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    n = k.shape[0]
+    if not (0 < n <= st.n_slots):
+        raise ValueError("write: n must be in 1..n_slots")
+    if k.shape != (n, st.n_heads, st.head_dim) or v.shape != k.shape or pos.shape != (n,):
+        raise ValueError("write: shape mismatch")
+    k_rot = rope(k, pos, st.rope_base)  # [n, H, D]
+    ck, sk = e4m3.quantize_rows(k_rot, st.margin)  # [n, H, D], [n, H]
+    cv, sv = e4m3.quantize_rows(v, st.margin)
+    slots = write_slots(st, n)
+    st.codes_k[:, slots, :] = np.transpose(ck, (1, 0, 2))
+    st.codes_v[:, slots, :] = np.transpose(cv, (1, 0, 2))
+    st.scale_k[:, slots] = sk.T
+    st.scale_v[:, slots] = sv.T
+    st.slot_pos[slots] = pos
+    st.head = int((st.head + n) % st.n_slots)
+    st.n_valid = int(min(st.n_valid + n, st.n_slots))
+
+
+def rotate(st: RingState, delta: int) -> None:
+    """Delta rotation at a position reset, in place, on every valid slot.
+
+    Each valid key (every head) is dequantized with its scale, each pair j is
+    rotated by phi_j = delta * omega_j, a new scale is taken from the rotated
+    key's amax, and the key is requantized.  slot_pos += delta.  V untouched.
+    """
+    slots = valid_slots(st)
+    if slots.size == 0:
+        return
+    c, s = delta_angles(st.head_dim, delta, st.rope_base)
+    x = e4m3.decode(st.codes_k[:, slots, :]) * st.scale_k[:, slots][..., None]
+    y = rotate_pairs(x, c, s)
+    ck, sk = e4m3.quantize_rows(y, st.margin)
+    st.codes_k[:, slots, :] = ck
+    st.scale_k[:, slots] = sk
+    st.slot_pos[slots] = st.slot_pos[slots] + delta
+
+
+def reset(st: RingState) -> None:
+    """Session reset: empty ring (head 0, no valid slots, positions 0)."""
+    st.head = 0
+    st.n_valid = 0
+    st.slot_pos[:] = 0
+
+
+def dequant_k(st: RingState) -> np.ndarray:
+    """Dequantized keys [H][N][D] float64."""
+    return e4m3.decode(st.codes_k) * st.scale_k[..., None]
+
+
+def dequant_v(st: RingState) -> np.ndarray:
+    """Dequantized values [H][N][D] float64."""
+    return e4m3.decode(st.codes_v) * st.scale_v[..., None]
