@@ -1,0 +1,310 @@
+// Ring-cache kernels for gfx950: buffer clear, session reset, the fused
+// RoPE + FP8 write, and the in-place delta rotation.
+//
+// Runway Characters paper: §4.1 (ring slots, device-side write position,
+// each slot keeps its written position), §4.2 and Appendix G (RoPE once at
+// write; at a reset every cached key is dequantized, rotated by the position
+// change and requantized; values untouched), §4.3 (K and V stored in e4m3,
+// only new tokens quantized), §4.4 (the pre-attention chain fused into one
+// pass per token).
+//
+// Both hot kernels are HBM-bound sweeps: every lane moves 16-byte vectors,
+// consecutive lanes cover consecutive bytes of a row, and the per-row amax
+// is a reduction across the lanes of that row (no LDS round trip except for
+// the V transpose).
+#include "rkv_launch.h"
+
+namespace rkv {
+
+// ---------------------------------------------------------------------------
+// Buffer clear (create) -- a kernel, not a memset node, so it can sit in a graph.
+__global__ void fill_zero_kernel(uint4* p, size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint4*)p, n16);
+  return hipGetLastError();
+}
+
+struct TurnsTable {
+  double t[kMaxHalfDim];
+};
+
+__global__ void init_consts_kernel(Geom g, TurnsTable tab, int n) {
+  double* dst = reinterpret_cast<double*>(g.base + g.consts);
+  if ((int)threadIdx.x < n) dst[threadIdx.x] = tab.t[threadIdx.x];
+}
+
+hipError_t launch_init_consts(const Geom& g, const double* turns, int n, hipStream_t s) {
+  TurnsTable tab{};
+  for (int j = 0; j < n && j < kMaxHalfDim; ++j) tab.t[j] = turns[j];
+  hipLaunchKernelGGL(init_consts_kernel, dim3(1), dim3(64), 0, s, g, tab, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Session reset: head = n_valid = 0 and every slot position = 0.
+__global__ void reset_kernel(Geom g, int layer_lo) {
+  const LayerPtrs L = layer_ptrs(g, layer_lo + (int)blockIdx.y);
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < g.n_pad) L.slot_pos[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x < 4) L.state[threadIdx.x] = 0;
+}
+
+hipError_t launch_reset(const Geom& g, int layer_lo, int layer_hi, hipStream_t s) {
+  dim3 grid((g.n_pad + 255) / 256, layer_hi - layer_lo);
+  hipLaunchKernelGGL(reset_kernel, grid, dim3(256), 0, s, g, layer_lo);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused write.  One workgroup per (16-slot group of the ring, head).  The
+// groups touched by a write of n tokens are consecutive (mod the group count
+// ceil(N/16), pad slots excluded) starting at the group holding `head`; a
+// contiguous run of n slots meets at most n/16 + 2 of them (one partial
+// group at each end, plus the short last group when it wraps).  The grid
+// covers that many and each thread works out from the device-side head whether its slot
+// is written and by which token: token i = (slot - head) mod N, written iff
+// i < n.  Thread (tau, lane) owns 8 elements of token row tau.
+template <int D>
+__global__ __launch_bounds__(16 * (D / 8)) void write_rope_fp8_kernel(
+    Geom g, int layer, const uint4* __restrict__ k, const uint4* __restrict__ v,
+    const int32_t* __restrict__ pos, int n) {
+  constexpr int LPR = D / 8;  // lanes per token row
+  __shared__ uint2 vcodes[16][LPR];
+
+  const LayerPtrs L = layer_ptrs(g, layer);
+  const int N = g.n_slots, NP = g.n_pad, H = g.n_heads;
+  const int head = L.state[0];
+  const int nvalid = L.state[1];
+  const int h = blockIdx.y;
+  const int NG = (N + 15) / 16;  // 16-slot groups of the ring (the last may be short)
+  const int G = (head / 16 + (int)blockIdx.x) % NG;
+  const int tau = threadIdx.x / LPR;
+  const int lane = threadIdx.x % LPR;
+  const int slot = 16 * G + tau;
+  int i = slot - head;
+  if (i < 0) i += N;
+  const bool active = slot < N && i < n;
+
+  uint4 kw = make_uint4(0u, 0u, 0u, 0u), vw = kw;
+  int32_t p = 0;
+  if (active) {
+    const size_t row = ((size_t)i * H + h) * LPR + lane;
+    kw = k[row];
+    vw = v[row];
+    p = pos[i];
+  }
+  float x[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
+                bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
+  float y[8];
+  const float u[8] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y),
+                      bf16_lo(vw.z), bf16_hi(vw.z), bf16_lo(vw.w), bf16_hi(vw.w)};
+  const double* turns = omega_turns(g);
+  float ak = 0.f, av = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float c = 1.f, s = 0.f;
+    if (active) rope_cs(p, turns[4 * lane + m], c, s);
+    y[2 * m] = x[2 * m] * c - x[2 * m + 1] * s;
+    y[2 * m + 1] = x[2 * m] * s + x[2 * m + 1] * c;
+    ak = fmaxf(ak, fmaxf(fabsf(y[2 * m]), fabsf(y[2 * m + 1])));
+    av = fmaxf(av, fmaxf(fabsf(u[2 * m]), fabsf(u[2 * m + 1])));
+  }
+  ak = group_max<LPR>(ak);
+  av = group_max<LPR>(av);
+  // scale s = fp32(margin * amax / 448); codes = e4m3(y / s)
+  const float sk = ak * g.margin / kE4M3Max, sv = av * g.margin / kE4M3Max;
+  const float rk = sk > 0.f ? 1.f / sk : 0.f;
+  const float rv = sv > 0.f ? 1.f / sv : 0.f;
+
+  uint2 ck, cv;
+  ck.x = pack2_fp8<false>(quant_div(y[0], sk, rk), quant_div(y[1], sk, rk), 0u);
+  ck.x = pack2_fp8<true>(quant_div(y[2], sk, rk), quant_div(y[3], sk, rk), ck.x);
+  ck.y = pack2_fp8<false>(quant_div(y[4], sk, rk), quant_div(y[5], sk, rk), 0u);
+  ck.y = pack2_fp8<true>(quant_div(y[6], sk, rk), quant_div(y[7], sk, rk), ck.y);
+  cv.x = pack2_fp8<false>(quant_div(u[0], sv, rv), quant_div(u[1], sv, rv), 0u);
+  cv.x = pack2_fp8<true>(quant_div(u[2], sv, rv), quant_div(u[3], sv, rv), cv.x);
+  cv.y = pack2_fp8<false>(quant_div(u[4], sv, rv), quant_div(u[5], sv, rv), 0u);
+  cv.y = pack2_fp8<true>(quant_div(u[6], sv, rv), quant_div(u[7], sv, rv), cv.y);
+
+  if (active) {
+    const size_t r = (size_t)h * NP + slot;
+    *reinterpret_cast<uint2*>(L.codes_k + r * D + 8 * lane) = ck;
+    if (lane == 0) {
+      L.scale_k[r] = sk;
+      L.scale_v[r] = sv;
+      if (h == 0) L.slot_pos[slot] = p;
+    }
+  }
+  vcodes[tau][lane] = cv;
+  __syncthreads();
+
+  // V: transposed 64-slot tiles, row d holds the tile's slots in order.  The
+  // group's 16 slots are 16 consecutive bytes of each row; thread t writes
+  // 8 of them (tokens 8*half .. 8*half+7) of row d.
+  {
+    const int t = threadIdx.x;
+    const int d = t >> 1, half = t & 1;
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(vcodes);
+    uint32_t b[8];
+    int nact = 0;
+    bool act[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tt = 8 * half + e;
+      b[e] = vb[tt * D + d];
+      const int sl = 16 * G + tt;
+      int ii = sl - head;
+      if (ii < 0) ii += N;
+      act[e] = sl < N && ii < n;
+      nact += act[e];
+    }
+    const int T = (16 * G) / kTile, w0 = (16 * G) % kTile;
+    uint8_t* dst = L.codes_v + (((size_t)h * g.n_tiles + T) * D + d) * kTile + w0 + 8 * half;
+    if (nact == 8) {
+      uint2 w;
+      w.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+      w.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+      *reinterpret_cast<uint2*>(dst) = w;
+    } else if (nact > 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (act[e]) dst[e] = (uint8_t)b[e];
+    }
+  }
+
+  // The last workgroup to finish advances the device-side write position.
+  // Every workgroup read head/n_valid before taking its ticket.
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const int total = gridDim.x * gridDim.y;
+    const int prev = atomicAdd(&L.state[2], 1);
+    if (prev == total - 1) {
+      L.state[0] = (int)(((long long)head + n) % N);
+      L.state[1] = nvalid + n < N ? nvalid + n : N;
+      L.state[2] = 0;
+      __threadfence();
+    }
+  }
+}
+
+hipError_t launch_write(const Geom& g, int layer, const void* k, const void* v, const int32_t* pos,
+                        int n, hipStream_t s) {
+  const int NG = (g.n_slots + 15) / 16;
+  int groups = (n + 15) / 16 + 2;
+  if (groups > NG) groups = NG;
+  dim3 grid(groups, g.n_heads);
+  if (g.head_dim == 128) {
+    hipLaunchKernelGGL(write_rope_fp8_kernel<128>, grid, dim3(256), 0, s, g, layer,
+                       (const uint4*)k, (const uint4*)v, pos, n);
+  } else {
+    hipLaunchKernelGGL(write_rope_fp8_kernel<64>, grid, dim3(128), 0, s, g, layer,
+                       (const uint4*)k, (const uint4*)v, pos, n);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Delta rotation.  One (slot, head) key row per D/16 lanes (16 codes each);
+// rows are visited in memory order (head-major, slot-minor) so each
+// workgroup streams a contiguous block of codes_k.  Only slots of the valid
+// cyclic range [head - n_valid, head) are touched.
+struct RotTable {
+  float c[kMaxHalfDim];
+  float s[kMaxHalfDim];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void rotate_kernel(Geom g, int layer_lo, int32_t delta,
+                                                    RotTable tab) {
+  constexpr int LPR = D / 16;
+  constexpr int RPW = 256 / LPR;
+  __shared__ float cs[D / 2], sn[D / 2];
+  if (threadIdx.x < D / 2) {
+    cs[threadIdx.x] = tab.c[threadIdx.x];
+    sn[threadIdx.x] = tab.s[threadIdx.x];
+  }
+  __syncthreads();
+
+  const LayerPtrs L = layer_ptrs(g, layer_lo + (int)blockIdx.y);
+  const int N = g.n_slots, NP = g.n_pad;
+  const int head = L.state[0], nv = L.state[1];
+  int a = head - nv;
+  if (a < 0) a += N;
+  const int row = blockIdx.x * RPW + threadIdx.x / LPR;
+  const int lane = threadIdx.x % LPR;
+  const int h = row / NP, slot = row % NP;
+  int rel = slot - a;
+  if (rel < 0) rel += N;
+  const bool valid = h < g.n_heads && slot < N && rel < nv;
+
+  uint4 w = make_uint4(0u, 0u, 0u, 0u);
+  float sc = 0.f;
+  const size_t r = (size_t)h * NP + slot;
+  if (valid) {
+    w = *reinterpret_cast<const uint4*>(L.codes_k + r * D + 16 * lane);
+    sc = L.scale_k[r];
+  }
+  float x[16];
+  unpack4_fp8(w.x, x[0], x[1], x[2], x[3]);
+  unpack4_fp8(w.y, x[4], x[5], x[6], x[7]);
+  unpack4_fp8(w.z, x[8], x[9], x[10], x[11]);
+  unpack4_fp8(w.w, x[12], x[13], x[14], x[15]);
+  float y[16];
+  float am = 0.f;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const float c = cs[8 * lane + m], s = sn[8 * lane + m];
+    const float x0 = x[2 * m] * sc, x1 = x[2 * m + 1] * sc;
+    y[2 * m] = x0 * c - x1 * s;
+    y[2 * m + 1] = x0 * s + x1 * c;
+    am = fmaxf(am, fmaxf(fabsf(y[2 * m]), fabsf(y[2 * m + 1])));
+  }
+  am = group_max<LPR>(am);
+  const float sn2 = am * g.margin / kE4M3Max;
+  const float rn = sn2 > 0.f ? 1.f / sn2 : 0.f;
+  uint4 o;
+  uint32_t* ow = &o.x;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t t = pack2_fp8<false>(quant_div(y[4 * q], sn2, rn), quant_div(y[4 * q + 1], sn2, rn), 0u);
+    ow[q] = pack2_fp8<true>(quant_div(y[4 * q + 2], sn2, rn), quant_div(y[4 * q + 3], sn2, rn), t);
+  }
+  if (valid) {
+    *reinterpret_cast<uint4*>(L.codes_k + r * D + 16 * lane) = o;
+    if (lane == 0) {
+      L.scale_k[r] = sn2;
+      if (h == 0) L.slot_pos[slot] += delta;
+    }
+  }
+}
+
+hipError_t launch_rotate(const Geom& g, int layer_lo, int layer_hi, int32_t delta,
+                         const float* cosv, const float* sinv, hipStream_t s) {
+  RotTable tab{};
+  const int half = g.head_dim / 2;
+  for (int j = 0; j < half; ++j) {
+    tab.c[j] = cosv[j];
+    tab.s[j] = sinv[j];
+  }
+  const int lpr = g.head_dim / 16;
+  const int rpw = 256 / lpr;
+  const long long rows = (long long)g.n_heads * g.n_pad;
+  dim3 grid((unsigned)((rows + rpw - 1) / rpw), layer_hi - layer_lo);
+  if (g.head_dim == 128)
+    hipLaunchKernelGGL(rotate_kernel<128>, grid, dim3(256), 0, s, g, layer_lo, delta, tab);
+  else
+    hipLaunchKernelGGL(rotate_kernel<64>, grid, dim3(256), 0, s, g, layer_lo, delta, tab);
+  return hipGetLastError();
+}
+
+}  // namespace rkv

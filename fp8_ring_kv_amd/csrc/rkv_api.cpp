@@ -1,0 +1,272 @@
+// C ABI of the ring KV cache: argument validation, buffer layout and kernel
+// launches.  No device allocation, no stream synchronization, no host read
+// of device state (see include/rkv.h).
+#include "rkv.h"
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "rkv_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return RKV_EHIP;
+}
+
+constexpr size_t kAlign = 256;
+constexpr size_t kConstsBytes = 4096;
+constexpr int kMaxSplits = 8;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+  rkv::Geom g;
+  rkv::AttnWs ws;  // pointers filled relative to base 0 (offsets) until create
+  size_t ws_qcodes, ws_qscale, ws_headc, ws_parto, ws_partml;
+  size_t total;
+};
+
+bool params_ok(const rkv_params* p, std::string* why) {
+  if (!p) return *why = "params is null", false;
+  if (p->n_layers < 1 || p->n_layers > 4096) return *why = "n_layers out of range [1, 4096]", false;
+  if (p->n_slots < 1 || p->n_slots > (1 << 20)) return *why = "n_slots out of range [1, 2^20]", false;
+  if (p->n_heads < 1 || p->n_heads > 256) return *why = "n_heads out of range [1, 256]", false;
+  if (p->head_dim != 64 && p->head_dim != 128) return *why = "head_dim must be 64 or 128", false;
+  if (p->max_queries < 1 || p->max_queries > (1 << 16))
+    return *why = "max_queries out of range [1, 2^16]", false;
+  if (p->precision != RKV_PRECISE && p->precision != RKV_FAST)
+    return *why = "precision must be RKV_PRECISE or RKV_FAST", false;
+  if (!(p->rope_base > 1.0f) || !std::isfinite(p->rope_base))
+    return *why = "rope_base must be finite and > 1", false;
+  if (!(p->scale_margin > 0.0f) || !(p->scale_margin <= 64.0f))
+    return *why = "scale_margin must be in (0, 64]", false;
+  return true;
+}
+
+Plan make_plan(const rkv_params* p) {
+  Plan pl{};
+  rkv::Geom& g = pl.g;
+  const size_t H = p->n_heads, D = p->head_dim;
+  const size_t NP = align_up((size_t)p->n_slots, rkv::kTile);
+  g.n_layers = p->n_layers;
+  g.n_slots = p->n_slots;
+  g.n_pad = (int32_t)NP;
+  g.n_tiles = (int32_t)(NP / rkv::kTile);
+  g.n_heads = p->n_heads;
+  g.head_dim = p->head_dim;
+  g.margin = p->scale_margin;
+  g.consts = 0;
+  g.layer0 = kConstsBytes;
+  size_t o = 0;
+  g.off_codes_k = o;
+  o = align_up(o + H * NP * D, kAlign);
+  g.off_codes_v = o;
+  o = align_up(o + H * NP * D, kAlign);
+  g.off_scale_k = o;
+  o = align_up(o + H * NP * 4, kAlign);
+  g.off_scale_v = o;
+  o = align_up(o + H * NP * 4, kAlign);
+  g.off_slot_pos = o;
+  o = align_up(o + NP * 4, kAlign);
+  g.off_state = o;
+  o = align_up(o + 16, kAlign);
+  g.layer_bytes = o;
+
+  size_t w = g.layer0 + (size_t)p->n_layers * g.layer_bytes;
+  const size_t nq_pad = align_up((size_t)p->max_queries, 32);
+  const size_t nqb = nq_pad / 32;
+  int splits = (int)((2 * 256 + nqb * H - 1) / (nqb * H));
+  if (splits < 1) splits = 1;
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  pl.ws.nq_pad = (int32_t)nq_pad;
+  pl.ws.splits = splits;
+  pl.ws.terms = p->precision == RKV_PRECISE ? 2 : 1;
+  pl.ws_qcodes = w;
+  w = align_up(w + 2 * H * nq_pad * D, kAlign);
+  pl.ws_qscale = w;
+  w = align_up(w + 2 * H * nq_pad, kAlign);
+  pl.ws_headc = w;
+  w = align_up(w + H * 4, kAlign);
+  const size_t units = nqb * H * (size_t)splits;
+  pl.ws_parto = w;
+  w = align_up(w + units * 32 * D * 4, kAlign);
+  pl.ws_partml = w;
+  w = align_up(w + units * 32 * 2 * 4, kAlign);
+  pl.total = w;
+  return pl;
+}
+
+}  // namespace
+
+struct rkv_cache {
+  rkv_params p;
+  rkv::Geom g;
+  rkv::AttnWs ws;
+  size_t bytes;
+  double half_turns[rkv::kMaxHalfDim];  // omega_j / (2 pi)
+  double omega[rkv::kMaxHalfDim];
+};
+
+extern "C" {
+
+const char* rkv_last_error(void) { return g_err.c_str(); }
+
+size_t ring_cache_bytes(const rkv_params* p) {
+  std::string why;
+  if (!params_ok(p, &why)) {
+    g_err = why;
+    return 0;
+  }
+  return make_plan(p).total;
+}
+
+int ring_cache_create(const rkv_params* p, void* dev_buf, size_t bytes, hipStream_t stream,
+                      rkv_cache** out) {
+  std::string why;
+  if (!out) return fail(RKV_EINVAL, "out is null");
+  *out = nullptr;
+  if (!params_ok(p, &why)) return fail(RKV_EINVAL, why);
+  if (!dev_buf) return fail(RKV_EINVAL, "dev_buf is null");
+  if (reinterpret_cast<uintptr_t>(dev_buf) % kAlign)
+    return fail(RKV_EINVAL, "dev_buf must be 256-byte aligned");
+  const Plan pl = make_plan(p);
+  if (bytes < pl.total)
+    return fail(RKV_EINVAL, "buffer too small: need " + std::to_string(pl.total) + " bytes");
+
+  rkv_cache* c = new (std::nothrow) rkv_cache();
+  if (!c) return fail(RKV_EINVAL, "out of host memory");
+  c->p = *p;
+  c->g = pl.g;
+  c->g.base = static_cast<uint8_t*>(dev_buf);
+  c->ws = pl.ws;
+  c->ws.qcodes = c->g.base + pl.ws_qcodes;
+  c->ws.qscale = c->g.base + pl.ws_qscale;
+  c->ws.head_c = reinterpret_cast<float*>(c->g.base + pl.ws_headc);
+  c->ws.part_o = reinterpret_cast<float*>(c->g.base + pl.ws_parto);
+  c->ws.part_ml = reinterpret_cast<float*>(c->g.base + pl.ws_partml);
+  c->bytes = pl.total;
+  const int half = p->head_dim / 2;
+  for (int j = 0; j < half; ++j) {
+    c->omega[j] = std::pow((double)p->rope_base, -2.0 * j / p->head_dim);
+    c->half_turns[j] = c->omega[j] / (2.0 * M_PI);
+  }
+  hipError_t e = rkv::launch_fill_zero(dev_buf, pl.total, stream);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "fill kernel launch");
+  }
+  e = rkv::launch_init_consts(c->g, c->half_turns, half, stream);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "init kernel launch");
+  }
+  *out = c;
+  g_err.clear();
+  return RKV_OK;
+}
+
+int ring_cache_destroy(rkv_cache* c) {
+  delete c;
+  return RKV_OK;
+}
+
+static int layer_range(const rkv_cache* c, int32_t layer, bool allow_all, int* lo, int* hi) {
+  if (layer == -1 && allow_all) {
+    *lo = 0;
+    *hi = c->p.n_layers;
+    return RKV_OK;
+  }
+  if (layer < 0 || layer >= c->p.n_layers)
+    return fail(RKV_EINVAL, "layer " + std::to_string(layer) + " out of range");
+  *lo = layer;
+  *hi = layer + 1;
+  return RKV_OK;
+}
+
+int ring_cache_reset(rkv_cache* c, int32_t layer, hipStream_t stream) {
+  if (!c) return fail(RKV_EINVAL, "cache is null");
+  int lo, hi;
+  if (int r = layer_range(c, layer, true, &lo, &hi)) return r;
+  hipError_t e = rkv::launch_reset(c->g, lo, hi, stream);
+  if (e != hipSuccess) return hip_fail(e, "reset kernel launch");
+  return RKV_OK;
+}
+
+int ring_cache_layout(const rkv_cache* c, int32_t layer, rkv_layout* out) {
+  if (!c) return fail(RKV_EINVAL, "cache is null");
+  if (!out) return fail(RKV_EINVAL, "out is null");
+  int lo, hi;
+  if (int r = layer_range(c, layer, false, &lo, &hi)) return r;
+  const size_t b = c->g.layer0 + (size_t)layer * c->g.layer_bytes;
+  out->codes_k = b + c->g.off_codes_k;
+  out->codes_v = b + c->g.off_codes_v;
+  out->scale_k = b + c->g.off_scale_k;
+  out->scale_v = b + c->g.off_scale_v;
+  out->slot_pos = b + c->g.off_slot_pos;
+  out->state = b + c->g.off_state;
+  out->layer_bytes = c->g.layer_bytes;
+  out->n_slots_padded = c->g.n_pad;
+  return RKV_OK;
+}
+
+static bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+int cache_write_rope_fp8(rkv_cache* c, int32_t layer, const void* k_bf16, const void* v_bf16,
+                         const int32_t* pos, int32_t n, hipStream_t stream) {
+  if (!c) return fail(RKV_EINVAL, "cache is null");
+  int lo, hi;
+  if (int r = layer_range(c, layer, false, &lo, &hi)) return r;
+  if (!k_bf16 || !v_bf16 || !pos) return fail(RKV_EINVAL, "null tensor pointer");
+  if (!aligned(k_bf16, 16) || !aligned(v_bf16, 16)) return fail(RKV_EINVAL, "k/v must be 16-byte aligned");
+  if (!aligned(pos, 4)) return fail(RKV_EINVAL, "pos must be 4-byte aligned");
+  if (n < 1 || n > c->p.n_slots)
+    return fail(RKV_EINVAL, "n = " + std::to_string(n) + " outside [1, n_slots]");
+  hipError_t e = rkv::launch_write(c->g, layer, k_bf16, v_bf16, pos, n, stream);
+  if (e != hipSuccess) return hip_fail(e, "write kernel launch");
+  return RKV_OK;
+}
+
+int cache_delta_rotate(rkv_cache* c, int32_t layer, int32_t delta, hipStream_t stream) {
+  if (!c) return fail(RKV_EINVAL, "cache is null");
+  int lo, hi;
+  if (int r = layer_range(c, layer, true, &lo, &hi)) return r;
+  float cs[rkv::kMaxHalfDim], sn[rkv::kMaxHalfDim];
+  const int half = c->p.head_dim / 2;
+  for (int j = 0; j < half; ++j) {
+    const double phi = (double)delta * c->omega[j];
+    cs[j] = (float)std::cos(phi);
+    sn[j] = (float)std::sin(phi);
+  }
+  hipError_t e = rkv::launch_rotate(c->g, lo, hi, delta, cs, sn, stream);
+  if (e != hipSuccess) return hip_fail(e, "rotate kernel launch");
+  return RKV_OK;
+}
+
+int cache_attend(rkv_cache* c, int32_t layer, const void* q_bf16, const int32_t* q_pos,
+                 int32_t n_q, void* out_bf16, hipStream_t stream) {
+  if (!c) return fail(RKV_EINVAL, "cache is null");
+  int lo, hi;
+  if (int r = layer_range(c, layer, false, &lo, &hi)) return r;
+  if (!q_bf16 || !q_pos || !out_bf16) return fail(RKV_EINVAL, "null tensor pointer");
+  if (!aligned(q_bf16, 16) || !aligned(out_bf16, 16))
+    return fail(RKV_EINVAL, "q/out must be 16-byte aligned");
+  if (!aligned(q_pos, 4)) return fail(RKV_EINVAL, "q_pos must be 4-byte aligned");
+  if (n_q < 1 || n_q > c->p.max_queries)
+    return fail(RKV_EINVAL, "n_q = " + std::to_string(n_q) + " outside [1, max_queries]");
+  hipError_t e = rkv::launch_attend(c->g, c->ws, layer, q_bf16, q_pos, n_q, out_bf16, stream);
+  if (e != hipSuccess) return hip_fail(e, "attend kernel launch");
+  return RKV_OK;
+}
+
+}  // extern "C"

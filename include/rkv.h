@@ -1,0 +1,155 @@
+/*
+ * rkv.h -- C ABI of the write-time FP8 ring KV cache for MI355X (gfx950).
+ *
+ * The operations follow "Runway Characters: Serving a 57B Video Diffusion
+ * Transformer for Real-Time Conversation" (arXiv:2611.05642):
+ *
+ *   ring cache with a device-side write position ....... §4.1
+ *   RoPE at write and a delta rotation at reset ........ §4.2, Appendix G
+ *   FP8 (e4m3) storage, only new tokens quantized ...... §4.3
+ *   fused pre-attention (RoPE + quantize + ring write) . §4.4
+ *   attention over the whole cache per call ........... §2 "The step budget",
+ *                                                        Appendix G
+ *   stacked allocation with per-layer views ........... §4.1
+ *   one configuration object with switches ............ §8 "Keep the plain path"
+ *
+ * Conventions shared by every call:
+ *
+ * - Memory.  The caller owns every device buffer: the cache buffer handed to
+ *   ring_cache_create and all inputs and outputs.  The library never
+ *   allocates device memory, never synchronizes a stream and never reads
+ *   device state on the host, so every call can be captured in a HIP graph
+ *   (no memset nodes are recorded; clears are done by kernels).
+ * - Streams.  Every call enqueues work on the given stream and returns.
+ *   Calls that touch the same cache must be ordered by the caller (same
+ *   stream, or events).  The attention workspace lives in the cache buffer
+ *   and is shared by all layers: two cache_attend calls on one cache must
+ *   not run concurrently.
+ * - Tensors.  bf16 tensors are contiguous [n][n_heads][head_dim] (row-major,
+ *   token-major), 16-byte aligned.  Positions are int32 device arrays.
+ * - Errors.  Misuse that the host can see (null pointer, layer or size out
+ *   of range, misaligned pointer, unsupported head_dim, buffer too small)
+ *   returns RKV_EINVAL and enqueues nothing; a failed kernel launch returns
+ *   RKV_EHIP.  rkv_last_error() gives a message for the calling thread.
+ *   Device-state conditions are defined, not errors: attention over an empty
+ *   cache writes zeros.
+ */
+#ifndef RKV_H
+#define RKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  RKV_OK = 0,
+  RKV_EINVAL = -1, /* bad argument; nothing was enqueued */
+  RKV_EHIP = -2,   /* a HIP call or kernel launch failed */
+};
+
+/* Attention precision (the config switch keeps the plain path, §8 "Keep the
+ * plain path behind every switch").
+ *   RKV_PRECISE: Q enters the FP8 products as two power-of-two-scaled e4m3
+ *                terms and the probabilities as two e4m3 terms (hi + lo/16).
+ *   RKV_FAST:    one term each (plain FP8 attention as in §4.3). */
+enum { RKV_PRECISE = 0, RKV_FAST = 1 };
+
+/* Cache configuration, fixed at create time. */
+typedef struct {
+  int32_t n_layers;    /* independent layer caches in one allocation (>= 1) */
+  int32_t n_slots;     /* ring slots per layer N (1 .. 1<<20) */
+  int32_t n_heads;     /* heads H (1 .. 256) */
+  int32_t head_dim;    /* D: 64 or 128 */
+  int32_t max_queries; /* largest n_q of one cache_attend call (1 .. 1<<16) */
+  int32_t precision;   /* RKV_PRECISE or RKV_FAST */
+  float rope_base;     /* RoPE base, omega_j = base^(-2j/D); 10000 */
+  float scale_margin;  /* scale s = margin * amax / 448; 1.0 */
+} rkv_params;
+
+/* Byte offsets into the cache buffer for one layer.  Layout (N_pad = N
+ * rounded up to 64; pad slots are zero and never valid):
+ *   codes_k  u8  [H][N_pad][D]        e4m3fn key codes, slot-major rows
+ *   codes_v  u8  [H][N_pad/64][D][64] e4m3fn value codes, transposed per
+ *                                      64-slot tile (byte w of row d = slot
+ *                                      64*tile + w)
+ *   scale_k  f32 [H][N_pad]           per-(slot, head) key scale
+ *   scale_v  f32 [H][N_pad]           per-(slot, head) value scale
+ *   slot_pos i32 [N_pad]              position each slot was written with
+ *   state    i32 [4]                  {head, n_valid, ticket, 0}: the next
+ *                                      write slot, the number of valid slots
+ *                                      (the cyclic range [head-n_valid, head)),
+ *                                      and a kernel-internal counter. */
+typedef struct {
+  size_t codes_k, codes_v, scale_k, scale_v, slot_pos, state;
+  size_t layer_bytes; /* distance between consecutive layers */
+  int32_t n_slots_padded;
+} rkv_layout;
+
+typedef struct rkv_cache rkv_cache; /* opaque host-side handle */
+
+/* Size in bytes of the cache buffer for these parameters (all layers, their
+ * state, and the attention workspace), or 0 if the parameters are invalid. */
+size_t ring_cache_bytes(const rkv_params* p);
+
+/* Create a handle over a caller-owned device buffer of at least
+ * ring_cache_bytes(p) bytes, 256-byte aligned.  Enqueues a kernel that
+ * zeroes the whole buffer on `stream` (an empty cache).  *out receives the
+ * handle.  The buffer must outlive the handle. */
+int ring_cache_create(const rkv_params* p, void* dev_buf, size_t bytes, hipStream_t stream,
+                      rkv_cache** out);
+
+/* Free the host handle (not the device buffer).  Null is accepted. */
+int ring_cache_destroy(rkv_cache* c);
+
+/* Session reset (§6 "Session start" clears the dynamic cache): set head,
+ * n_valid and every slot position of one layer (or all layers when
+ * layer == -1) to zero.  Codes and scales are left as they are; slots
+ * outside the valid range are never read. */
+int ring_cache_reset(rkv_cache* c, int32_t layer, hipStream_t stream);
+
+/* Fill *out with the byte offsets of `layer` inside the cache buffer. */
+int ring_cache_layout(const rkv_cache* c, int32_t layer, rkv_layout* out);
+
+/* Ring write with RoPE and FP8 quantization fused (§4.1, §4.2, §4.3, §4.4).
+ * k_bf16, v_bf16: [n][H][D] bf16 device tensors of the n new tokens.
+ * pos: [n] int32 device positions.  Token i goes to slot
+ * (head + i) mod N; its key is rotated at pos[i] (interleaved pairs
+ * (2j, 2j+1), angle pos[i] * base^(-2j/D) computed in double precision),
+ * then key and value rows are quantized per (token, head):
+ * s = fp32(margin * amax / 448), code = e4m3(y / s) rounded to nearest even,
+ * saturating at +-448.  slot_pos[slot] = pos[i].  Afterwards, on the device,
+ * head <- (head + n) mod N and n_valid <- min(n_valid + n, N).
+ * Requires 1 <= n <= N. */
+int cache_write_rope_fp8(rkv_cache* c, int32_t layer, const void* k_bf16, const void* v_bf16,
+                         const int32_t* pos, int32_t n, hipStream_t stream);
+
+/* Delta rotation at a position reset (§4.2, Appendix G): for every valid
+ * slot of `layer` (all layers when layer == -1) and every head, dequantize
+ * the key, rotate pair j by delta * base^(-2j/D) in fp32 (cos and sin taken
+ * in double precision), take a new scale from the rotated key's amax and
+ * requantize in place; slot_pos += delta.  Values are not touched. */
+int cache_delta_rotate(rkv_cache* c, int32_t layer, int32_t delta, hipStream_t stream);
+
+/* Attention of n_q new queries over every valid slot of `layer` (§2,
+ * §4.3, Appendix G).  q_bf16: [n_q][H][D] bf16 device tensor; q_pos: [n_q]
+ * int32 device positions (RoPE is applied to Q here, at q_pos).  out_bf16:
+ * [n_q][H][D] bf16 device tensor receiving softmax(q k^T / sqrt(D)) v over
+ * the dequantized cache, computed with FP8 matrix instructions in the
+ * configured precision, rounded to nearest even.  Non-causal.  An empty
+ * cache gives zeros.  Requires 1 <= n_q <= max_queries. */
+int cache_attend(rkv_cache* c, int32_t layer, const void* q_bf16, const int32_t* q_pos,
+                 int32_t n_q, void* out_bf16, hipStream_t stream);
+
+/* Message for the last error on the calling thread ("" if none). */
+const char* rkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RKV_H */

@@ -1,0 +1,99 @@
+"""C ABI checks that need no GPU: the library loads into torch's HIP runtime,
+exports every function include/rkv.h declares, and rejects host-visible
+misuse with RKV_EINVAL before enqueueing anything.  No call here reaches a
+kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_ring_kv_amd as rkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_library_is_built():
+    assert os.path.exists(rkv.lib_path()), "run `python -m fp8_ring_kv_amd.build` first"
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) >= {"ring_cache_bytes", "ring_cache_create", "ring_cache_destroy",
+                          "ring_cache_reset", "ring_cache_layout", "cache_write_rope_fp8",
+                          "cache_delta_rotate", "cache_attend", "rkv_last_error"}
+    L = rkv.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_single_hip_runtime_in_process():
+    rkv.lib()
+    maps = open("/proc/self/maps").read()
+    libs = sorted(set(re.findall(r"\S*libamdhip64\.so\S*", maps)))
+    assert len(libs) == 1, libs
+
+
+def params(**kw):
+    base = dict(n_layers=1, n_slots=5788, n_heads=12, head_dim=128, max_queries=757,
+                precision=rkv.RKV_PRECISE, rope_base=10000.0, scale_margin=1.0)
+    base.update(kw)
+    return rkv.rkv_params(**base)
+
+
+def test_bytes_cover_the_layout():
+    p = params()
+    nb = rkv.ring_cache_bytes(p)
+    np_ = 5824  # 5788 rounded up to 64
+    per_layer = 2 * 12 * np_ * 128 + 2 * 12 * np_ * 4 + np_ * 4 + 16
+    assert nb > per_layer
+    p60 = params(n_layers=60)
+    assert rkv.ring_cache_bytes(p60) - nb >= 59 * per_layer
+    assert nb % 256 == 0
+
+
+@pytest.mark.parametrize("field,value", [
+    ("n_layers", 0), ("n_slots", 0), ("n_slots", (1 << 20) + 1), ("n_heads", 0),
+    ("head_dim", 96), ("head_dim", 256), ("max_queries", 0), ("precision", 7),
+    ("rope_base", 1.0), ("rope_base", float("inf")), ("scale_margin", 0.0),
+])
+def test_invalid_params_give_zero_bytes_and_einval(field, value):
+    p = params(**{field: value})
+    assert rkv.ring_cache_bytes(p) == 0
+    assert rkv.rkv_last_error() != ""
+    h = ctypes.c_void_p()
+    rc = rkv.lib().ring_cache_create(ctypes.byref(p), ctypes.c_void_p(1 << 20), 1 << 40, None, ctypes.byref(h))
+    assert rc == rkv.RKV_EINVAL and h.value is None
+
+
+def test_create_rejects_bad_buffers_without_launching():
+    p = params()
+    nb = rkv.ring_cache_bytes(p)
+    L = rkv.lib()
+    h = ctypes.c_void_p()
+    assert L.ring_cache_create(ctypes.byref(p), None, nb, None, ctypes.byref(h)) == rkv.RKV_EINVAL
+    assert L.ring_cache_create(ctypes.byref(p), ctypes.c_void_p(0x1000 + 16), nb, None,
+                               ctypes.byref(h)) == rkv.RKV_EINVAL
+    assert "aligned" in rkv.rkv_last_error()
+    assert L.ring_cache_create(ctypes.byref(p), ctypes.c_void_p(0x1000), nb - 256, None,
+                               ctypes.byref(h)) == rkv.RKV_EINVAL
+    assert "too small" in rkv.rkv_last_error()
+    assert L.ring_cache_create(ctypes.byref(p), ctypes.c_void_p(0x1000), nb, None, None) == rkv.RKV_EINVAL
+
+
+def test_calls_on_null_cache_are_einval():
+    L = rkv.lib()
+    assert L.cache_write_rope_fp8(None, 0, None, None, None, 1, None) == rkv.RKV_EINVAL
+    assert L.cache_delta_rotate(None, 0, 5, None) == rkv.RKV_EINVAL
+    assert L.cache_attend(None, 0, None, None, 1, None, None) == rkv.RKV_EINVAL
+    assert L.ring_cache_reset(None, -1, None) == rkv.RKV_EINVAL
+    assert L.ring_cache_layout(None, 0, None) == rkv.RKV_EINVAL
+    assert L.ring_cache_destroy(None) == rkv.RKV_OK

@@ -1,0 +1,234 @@
+"""GPU parity of cache_attend against the oracle.
+
+Gates (the hot path's float contract, max-abs 2e-2 / mean-abs 2e-3 on bf16
+outputs against an fp64 oracle on the dequantized cache):
+
+* precise mode (two-term Q and P, the default) vs ``attend_exact``: errors
+  divided by max(1, sigma_v[head, channel]) within 2e-2 max / 2e-3 mean on
+  every workload; raw errors within the same bounds on N(0,1) workloads
+  (where sigma_v ~ 1 the two coincide);
+* precise mode vs ``attend_emul`` (its declared numerics): same bounds;
+* fast mode (single-term) vs ``attend_emul(q_terms=1, p_terms=1)`` and, on
+  N(0,1) data, raw vs ``attend_exact``.
+
+The outputs of bf16 rounding alone reach the raw bound on channels whose
+values are ~8x larger (outlier channels), which is why errors are
+normalized per output channel.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_ring_kv_amd as rkv
+from oracle import attend as oatt, ring as oring
+from oracle.bf16 import round_bf16
+from tests.gpu_common import DEV, attn_errors, pos_dev, require_gpu, to_dev
+from workloads import ATTEND, STRESS, TINY, Bf16, Config, OutlierSpec, Stream, positions
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def gate(name, gpu, ref, sigma, max_tol=2e-2, mean_tol=2e-3, raw=False):
+    rmax, rmean, nmax, nmean = attn_errors(gpu, ref, sigma)
+    print(f"{name}: raw max {rmax:.2e} mean {rmean:.2e} | norm max {nmax:.2e} mean {nmean:.2e}")
+    assert nmax < max_tol and nmean < mean_tol, name
+    if raw:
+        assert rmax < max_tol and rmean < mean_tol, name + " (raw)"
+    return rmax, rmean, nmax, nmean
+
+
+def sub_heads(x: Bf16, heads) -> Bf16:
+    return Bf16(np.ascontiguousarray(x.bits[:, heads]), np.ascontiguousarray(x.f64[:, heads]))
+
+
+def oracle_state(cfg, heads):
+    return oring.RingState(cfg.n_slots, len(heads), cfg.head_dim, cfg.rope_base)
+
+
+def gpu_out(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("precision", [rkv.RKV_PRECISE, rkv.RKV_FAST])
+def test_tiny_session(precision):
+    cfg = TINY
+    cache = rkv.RingCache(1, cfg.n_slots, 1, 64, 16, precision, device=DEV)
+    st = oring.RingState(cfg.n_slots, 1, 64)
+    s = Stream(cfg)
+    terms = 2 if precision == rkv.RKV_PRECISE else 1
+    chunks = []
+    for c in range(6):
+        q, k, v = s.chunk()
+        pos = positions(16 * c, 16)
+        cache.write(0, to_dev(k), to_dev(v), pos_dev(pos))
+        oring.write(st, k.f64, v.f64, pos)
+        chunks.append((q, pos))
+        out = gpu_out(cache.attend(0, to_dev(q), pos_dev(pos)))
+        sig = oatt.sigma_v(st)
+        emul = round_bf16(oatt.attend_emul(st, q.f64, pos, terms, terms))
+        gate(f"tiny[{c}] vs emul", out, emul, sig)
+        if precision == rkv.RKV_PRECISE:
+            gate(f"tiny[{c}] vs exact", out, oatt.attend_exact(st, q.f64, pos), sig, raw=True)
+    cache.rotate(0, -80)
+    oring.rotate(st, -80)
+    q, pos = chunks[5]
+    out = gpu_out(cache.attend(0, to_dev(q), pos_dev(pos - 80)))
+    emul = round_bf16(oatt.attend_emul(st, q.f64, pos - 80, terms, terms))
+    gate("tiny after reset vs emul", out, emul, oatt.sigma_v(st))
+
+
+def build_attend_cache(cfg, heads_checked, precision=rkv.RKV_PRECISE, total=8888, max_q=757):
+    """Write `total` tokens in chunks of 757 (the last shorter); returns the GPU
+    cache, the oracle state for `heads_checked`, and the token stream."""
+    cache = rkv.RingCache(1, cfg.n_slots, cfg.n_heads, cfg.head_dim, max_q, precision, device=DEV)
+    st = oracle_state(cfg, heads_checked)
+    s = Stream(cfg)
+    p0 = 0
+    while p0 < total:
+        n = min(757, total - p0)
+        _, k, v = s.chunk(n)
+        pos = positions(p0, n)
+        cache.write(0, to_dev(k), to_dev(v), pos_dev(pos))
+        oring.write(st, sub_heads(k, heads_checked).f64, sub_heads(v, heads_checked).f64, pos)
+        p0 += n
+    return cache, st, s
+
+
+def test_attend_workload_full_size_sampled():
+    """757 queries x 5,788 slots x 12 heads, ring head at slot 3,100, 2% outliers x8.
+
+    The GPU computes every output; the oracle checks 3 heads on 160 sampled rows."""
+    cfg = ATTEND
+    heads = [0, 5, 11]
+    cache, st, s = build_attend_cache(cfg, heads)
+    torch.cuda.synchronize()
+    assert int(cache.state(0)[0]) == 3100 and int(cache.state(0)[1]) == 5788
+    assert st.head == 3100
+    q, _, _ = s.chunk(757)
+    qpos = positions(8131, 757)
+    out = gpu_out(cache.attend(0, to_dev(q), pos_dev(qpos)))
+    rows = np.unique(np.concatenate([np.arange(0, 757, 5), [756, 755, 31, 32, 33]]))
+    qs = sub_heads(Bf16(q.bits[rows], q.f64[rows]), heads)
+    sig = oatt.sigma_v(st)
+    ex = oatt.attend_exact(st, qs.f64, qpos[rows])
+    em = round_bf16(oatt.attend_emul(st, qs.f64, qpos[rows]))
+    g = out[rows][:, heads]
+    gate("C2 vs exact (normalized)", g, ex, sig)
+    gate("C2 vs emul", g, em, sig)
+    assert np.all(np.isfinite(out))
+
+
+def test_attend_fast_mode_on_unit_normal_data():
+    cfg = Config("attend_n01", n_heads=4, head_dim=128, n_slots=5788, chunk=757, seed=21)
+    heads = [0, 1, 2, 3]
+    cache, st, s = build_attend_cache(cfg, heads, precision=rkv.RKV_FAST, total=6000)
+    q, _, _ = s.chunk(200)
+    qpos = positions(5800, 200)
+    out = gpu_out(cache.attend(0, to_dev(q), pos_dev(qpos)))
+    sig = oatt.sigma_v(st)
+    gate("fast vs exact raw (N(0,1))", out, oatt.attend_exact(st, q.f64, qpos), sig, raw=True)
+    gate("fast vs emul(1,1)", out, round_bf16(oatt.attend_emul(st, q.f64, qpos, 1, 1)), sig)
+
+
+def test_empty_cache_gives_zeros():
+    cache = rkv.RingCache(1, 128, 2, 128, 40, device=DEV)
+    q = torch.randn(40, 2, 128, device=DEV).to(torch.bfloat16)
+    out = cache.attend(0, q, torch.arange(40, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert not out.float().abs().sum().item()
+
+
+def test_one_valid_slot_returns_its_value():
+    cfg = Config("one", n_heads=2, head_dim=128, n_slots=500, chunk=1, seed=9)
+    cache = rkv.RingCache(1, 500, 2, 128, 33, device=DEV)
+    st = oring.RingState(500, 2, 128)
+    s = Stream(cfg)
+    _, k, v = s.chunk(1)
+    cache.write(0, to_dev(k), to_dev(v), pos_dev([7]))
+    oring.write(st, k.f64, v.f64, [7])
+    q, _, _ = s.chunk(33)
+    out = gpu_out(cache.attend(0, to_dev(q), pos_dev(np.arange(33))))
+    want = round_bf16(oring.dequant_v(st)[:, 0, :])[None].repeat(33, axis=0)
+    assert np.max(np.abs(out - want) / np.maximum(np.abs(want), 1e-3)) <= 2 ** -7
+
+
+def test_partial_fill_masks_invalid_slots():
+    """A 2,000-slot ring holding 757 tokens whose valid range straddles a 64-slot tile."""
+    cfg = Config("partial", n_heads=3, head_dim=128, n_slots=2000, chunk=0, seed=10,
+                 outliers=OutlierSpec(0.02, 8.0))
+    cache = rkv.RingCache(1, 2000, 3, 128, 100, device=DEV)
+    st = oring.RingState(2000, 3, 128)
+    s = Stream(cfg)
+    for n, p0 in [(37, 0), (757, 37)]:
+        _, k, v = s.chunk(n)
+        cache.write(0, to_dev(k), to_dev(v), pos_dev(positions(p0, n)))
+        oring.write(st, k.f64, v.f64, positions(p0, n))
+    q, _, _ = s.chunk(100)
+    qpos = positions(700, 100)
+    out = gpu_out(cache.attend(0, to_dev(q), pos_dev(qpos)))
+    sig = oatt.sigma_v(st)
+    gate("partial vs exact", out, oatt.attend_exact(st, q.f64, qpos), sig)
+
+
+def test_wrapped_ring_equals_linear_cache():
+    """Same tokens, one cache wrapped (head mid-ring), one written from slot 0."""
+    cfg = Config("wrap", n_heads=2, head_dim=128, n_slots=1500, chunk=0, seed=11)
+    s = Stream(cfg)
+    toks = [s.chunk(n) for n in (700, 700, 700)]
+    wrapped = rkv.RingCache(1, 1500, 2, 128, 64, device=DEV)
+    linear = rkv.RingCache(1, 1500, 2, 128, 64, device=DEV)
+    p0 = 0
+    for _, k, v in toks:
+        wrapped.write(0, to_dev(k), to_dev(v), pos_dev(positions(p0, 700)))
+        p0 += 700
+    # the wrapped ring keeps tokens 600 .. 2099 (positions 600..2099); write those linearly
+    ks = np.concatenate([t[1].bits for t in toks])[600:]
+    vs = np.concatenate([t[2].bits for t in toks])[600:]
+    linear.write(0, to_dev(Bf16(ks, None)), to_dev(Bf16(vs, None)), pos_dev(positions(600, 1500)))
+    q, _, _ = s.chunk(64)
+    qpos = positions(2100, 64)
+    a = gpu_out(wrapped.attend(0, to_dev(q), pos_dev(qpos)))
+    b = gpu_out(linear.attend(0, to_dev(q), pos_dev(qpos)))
+    torch.cuda.synchronize()
+    assert int(wrapped.state(0)[0]) == 600 and int(linear.state(0)[0]) == 0
+    assert np.max(np.abs(a - b)) < 2e-2 and np.mean(np.abs(a - b)) < 1e-3
+
+
+def test_stress_partial_fill_sessions():
+    """48 heads x 11,576 slots, 1% outliers x16, attends while the ring fills, one reset."""
+    cfg = STRESS
+    heads = [3, 47]
+    cache = rkv.RingCache(1, cfg.n_slots, cfg.n_heads, 128, 757, device=DEV)
+    st = oracle_state(cfg, heads)
+    s = Stream(cfg)
+    rows = np.arange(0, 757, 11)
+    for w in range(24):
+        q, k, v = s.chunk()
+        pos = positions(757 * w, 757)
+        if w == 21:
+            d = -21 * 757
+            cache.rotate(0, d)
+            oring.rotate(st, d)
+        p = pos - (21 * 757 if w >= 21 else 0)
+        cache.write(0, to_dev(k), to_dev(v), pos_dev(p))
+        oring.write(st, sub_heads(k, heads).f64, sub_heads(v, heads).f64, p)
+        if w in (0, 1, 7, 15, 16, 21, 23):
+            out = gpu_out(cache.attend(0, to_dev(q), pos_dev(p)))
+            qs = sub_heads(Bf16(q.bits[rows], q.f64[rows]), heads)
+            ex = oatt.attend_exact(st, qs.f64, p[rows])
+            gate(f"stress write {w} (valid {st.n_valid})", out[rows][:, heads], ex, oatt.sigma_v(st))
+
+
+def test_attend_rejects_bad_arguments():
+    cache = rkv.RingCache(1, 64, 1, 64, 16, device=DEV)
+    q = torch.zeros(17, 1, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(rkv.RkvError):
+        cache.attend(0, q, torch.zeros(17, dtype=torch.int32, device=DEV))  # n_q > max_queries
+    with pytest.raises(rkv.RkvError):
+        cache.attend(3, q[:4], torch.zeros(4, dtype=torch.int32, device=DEV))
