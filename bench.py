@@ -1,0 +1,260 @@
+"""Benchmark of the write-time FP8 ring KV hot path on one MI355X.
+
+One step is the per-call cache work of a block forward in the pages'
+workload (Runway Characters paper, §2 "The step budget", §4, Appendix G):
+write the 757 new tokens of the chunk into the 5,788-slot ring (RoPE + FP8
+quantization fused), then attend the chunk's 757 queries over every slot,
+12 heads x 128 (one GPU's head share).  Every 42nd step is preceded by the
+position reset: a delta rotation of every cached key by -42 * 757.  The
+cache starts full with its ring head at slot 3,100 (8,888 tokens written).
+
+Prints one JSON line.  `value` is microseconds per step (= per attention call
+with its cache work, resets amortized).  Per-operation times come from
+separate HIP-event-timed loops on the launch stream; `roofline` is the
+attention call (the dominant cost) against the dense FP8 matrix peak.
+`cpu_baseline` times the NumPy float64 oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+H, D, N, CHUNK, RESET_EVERY = 12, 128, 5788, 757, 42
+ATTN_FLOP = 4.0 * CHUNK * N * H * D  # QK^T and PV, 2 flops per multiply-add
+WRITE_BYTES = (6 * H * D + 8 * H + 4) * CHUNK  # bf16 K,V in; e4m3 K,V + 2 scales + pos out
+ROTATE_BYTES = (2 * H * D + 8 * H + 8) * N  # codes r/w, scale r/w, position r/w
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=84)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--precision", choices=["precise", "fast"], default="precise")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--reps", type=int, default=200, help="launches per component loop")
+    ap.add_argument("--workgroups", type=int, default=0,
+                    help="persistent workgroups per attention call (0 = one per compute unit)")
+    return ap.parse_args()
+
+
+def to_dev(x):
+    """bf16 bit patterns (workloads.Bf16) -> device bf16 tensor."""
+    import torch
+    return torch.from_numpy(x.bits.view(np.int16).copy()).view(torch.bfloat16).to("cuda:0")
+
+
+def timed(fn, reps, stream):
+    """Average milliseconds of fn() over `reps` launches, bracketed by events on `stream`."""
+    import torch
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def cpu_baseline():
+    """The oracle on a bounded sample: one 757-token write (12 heads), attention of
+    the 757 queries on 2 of the 12 heads (scaled by 6), one-layer rotation / 42."""
+    from threadpoolctl import threadpool_info
+    from oracle import attend as oatt, ring as oring
+    from workloads import ATTEND, Stream, positions
+    st = oring.RingState(N, H, D)
+    s = Stream(ATTEND)
+    p0 = 0
+    while p0 < 8888:
+        n = min(CHUNK, 8888 - p0)
+        _, k, v = s.chunk(n)
+        oring.write(st, k.f64, v.f64, positions(p0, n))
+        p0 += n
+    q, k, v = s.chunk()
+    pos = positions(8888, CHUNK)
+    t0 = time.perf_counter()
+    oring.write(st, k.f64, v.f64, pos)
+    t_write = time.perf_counter() - t0
+    sub = oring.RingState(N, 2, D, head=st.head, n_valid=st.n_valid, slot_pos=st.slot_pos,
+                          codes_k=st.codes_k[:2], codes_v=st.codes_v[:2],
+                          scale_k=st.scale_k[:2], scale_v=st.scale_v[:2])
+    t0 = time.perf_counter()
+    oatt.attend_exact(sub, q.f64[:, :2], pos)
+    t_attend = (time.perf_counter() - t0) * H / 2
+    t0 = time.perf_counter()
+    oring.rotate(st, -RESET_EVERY * CHUNK)
+    t_rot = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    per_step = t_write + t_attend + t_rot / RESET_EVERY
+    return {
+        "value": per_step * 1e6,
+        "unit": "us per step",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": ("NumPy float64 oracle on the host: one 757-token write (12 heads), "
+                   "attend_exact of the 757 queries on 2 of 12 heads scaled x6, one full "
+                   "5,788-slot rotation amortized over 42 steps"),
+        "parts_s": {"write": t_write, "attend_12h_est": t_attend, "rotate": t_rot},
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+    import torch
+    import fp8_ring_kv_amd as rkv
+    from workloads import ATTEND, Stream, positions
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    prec = rkv.RKV_PRECISE if args.precision == "precise" else rkv.RKV_FAST
+    cache = rkv.RingCache(1, N, H, D, CHUNK, prec, device=dev, attn_workgroups=args.workgroups)
+
+    # starting state: 8,888 tokens written in 757-token chunks -> ring head at slot 3,100
+    s = Stream(ATTEND)
+    p0 = 0
+    while p0 < 8888:
+        n = min(CHUNK, 8888 - p0)
+        _, k, v = s.chunk(n)
+        cache.write(0, to_dev(k), to_dev(v), torch.from_numpy(positions(p0, n)).to(dev))
+        p0 += n
+    torch.cuda.synchronize()
+    assert int(cache.state(0)[0]) == 3100 and int(cache.state(0)[1]) == N
+
+    # input pool resident in HBM before timing: RESET_EVERY chunks of q, k, v
+    pool = []
+    for _ in range(RESET_EVERY):
+        q, k, v = s.chunk()
+        pool.append((to_dev(q), to_dev(k), to_dev(v)))
+    pos_base = torch.arange(CHUNK, dtype=torch.int32, device=dev)
+    out = torch.empty(CHUNK, H, D, dtype=torch.bfloat16, device=dev)
+    # positions of the 42 chunks of a reset period (after each reset the cached
+    # positions move back by 42 * 757, so new chunks reuse the same ones)
+    pos_pool = [pos_base + (8888 + CHUNK * j) for j in range(RESET_EVERY)]
+
+    def step_fast(i):
+        j = i % RESET_EVERY
+        if j == 0 and i > 0:
+            cache.rotate(0, -RESET_EVERY * CHUNK)
+        q, k, v = pool[j]
+        cache.write(0, k, v, pos_pool[j])
+        cache.attend(0, q, pos_pool[j], out)
+
+    for i in range(args.warmup):
+        step_fast(i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    t_host0 = time.perf_counter()
+    a.record(stream)
+    for i in range(args.steps):
+        step_fast(args.warmup + i)
+    b.record(stream)
+    b.synchronize()
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - t_host0
+    ms_per_step = a.elapsed_time(b) / args.steps
+    assert torch.isfinite(out.float()).all()
+
+    comp = {}
+    if not args.no_components:
+        r = args.reps
+        q0, k0, v0 = pool[0]
+        comp["attend_us"] = 1e3 * timed(lambda: cache.attend(0, q0, pos_pool[0], out), r, stream)
+        comp["write_us"] = 1e3 * timed(lambda: cache.write(0, k0, v0, pos_pool[0]), r, stream)
+        flip = [1]
+
+        def rot():
+            cache.rotate(0, flip[0])
+            flip[0] = -flip[0]
+        comp["rotate_1layer_us"] = 1e3 * timed(rot, max(20, r // 4), stream)
+        comp["write_GBps"] = WRITE_BYTES / comp["write_us"] / 1e3
+        comp["rotate_1layer_GBps"] = ROTATE_BYTES / comp["rotate_1layer_us"] / 1e3
+        comp["attend_TFLOPs"] = ATTN_FLOP / comp["attend_us"] / 1e6
+        # 60 stacked layer caches (1.1 GB): rotation of every layer in one launch,
+        # and writes cycling over the layers -- both far beyond the 256 MB cache
+        big = rkv.RingCache(60, N, H, D, CHUNK, prec, device=dev)
+        for layer in range(60):
+            for c in range(8):
+                q, k, v = pool[(layer + c) % RESET_EVERY]
+                big.write(layer, k, v, pos_pool[c])
+        torch.cuda.synchronize()
+        flip60 = [1]
+
+        def rot60():
+            big.rotate(-1, flip60[0])
+            flip60[0] = -flip60[0]
+        comp["rotate_60layer_us"] = 1e3 * timed(rot60, 6, stream)
+        comp["rotate_60layer_GBps"] = 60 * ROTATE_BYTES / comp["rotate_60layer_us"] / 1e3
+        lay = [0]
+
+        def wr60():
+            q, k, v = pool[lay[0] % RESET_EVERY]
+            big.write(lay[0] % 60, k, v, pos_pool[0])
+            lay[0] += 1
+        comp["write_60layer_cycling_us"] = 1e3 * timed(wr60, 240, stream)
+        comp["write_60layer_cycling_GBps"] = WRITE_BYTES / comp["write_60layer_cycling_us"] / 1e3
+        del big
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": "µs per attention call (757q×5788 FP8 KV) + cache-write GB/s; % of roofline",
+        "value": round(ms_per_step * 1e3, 3),
+        "unit": "us per call (write 757 tokens + attend 757 queries; resets amortized)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 matmul, fp32 softmax/accumulate",
+        "data": "synthetic",
+        "config": {"workload": "attend_757x5788_h12", "heads": H, "head_dim": D, "slots": N,
+                   "new_tokens": CHUNK, "queries": CHUNK, "reset_every": RESET_EVERY,
+                   "ring_head_start": 3100, "precision": args.precision,
+                   "outliers": "2% of channels x8"},
+        "host_wall_s": round(host_s, 4),
+    }
+    if comp:
+        res["components"] = {k: round(v, 4) for k, v in comp.items()}
+        res["write_GBps"] = round(comp["write_GBps"], 2)
+        achieved = comp["attend_TFLOPs"]
+        res["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2),
+                           "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                           "kernel": "cache_attend (q_prep + attend + combine)",
+                           "per_launch_flop": ATTN_FLOP,
+                           "per_launch_us": round(comp["attend_us"], 3)}
+        res["roofline_hbm"] = {
+            "write": {"achieved": round(comp["write_GBps"], 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                      "frac": round(comp["write_GBps"] / PEAK_HBM_GBPS, 4), "bytes": WRITE_BYTES},
+            "rotate_60layer": {"achieved": round(comp["rotate_60layer_GBps"], 1), "peak": PEAK_HBM_GBPS,
+                               "unit": "GB/s", "frac": round(comp["rotate_60layer_GBps"] / PEAK_HBM_GBPS, 4),
+                               "bytes": 60 * ROTATE_BYTES},
+        }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -46,6 +46,7 @@ class rkv_params(ctypes.Structure):
         ("precision", ctypes.c_int32),
         ("rope_base", ctypes.c_float),
         ("scale_margin", ctypes.c_float),
+        ("attn_workgroups", ctypes.c_int32),
     ]
 
 
@@ -57,6 +58,7 @@ class rkv_layout(ctypes.Structure):
         ("scale_v", ctypes.c_size_t),
         ("slot_pos", ctypes.c_size_t),
         ("state", ctypes.c_size_t),
+        ("vmax", ctypes.c_size_t),
         ("layer_bytes", ctypes.c_size_t),
         ("n_slots_padded", ctypes.c_int32),
     ]
@@ -181,9 +183,9 @@ class RingCache:
 
     def __init__(self, n_layers: int, n_slots: int, n_heads: int, head_dim: int, max_queries: int,
                  precision: int = RKV_PRECISE, rope_base: float = 10000.0, scale_margin: float = 1.0,
-                 device: str | torch.device = "cuda", stream=None):
+                 device: str | torch.device = "cuda", stream=None, attn_workgroups: int = 0):
         self.params = rkv_params(n_layers, n_slots, n_heads, head_dim, max_queries, precision,
-                                 rope_base, scale_margin)
+                                 rope_base, scale_margin, attn_workgroups)
         nbytes = ring_cache_bytes(self.params)
         if nbytes == 0:
             raise RkvError(RKV_EINVAL, "ring_cache_bytes")
@@ -246,6 +248,11 @@ class RingCache:
         """(head, n_valid, ticket, 0) int32 on device."""
         lay = self.layout(layer)
         return self._view(lay.state, 16, torch.int32)
+
+    def vmax(self, layer: int) -> torch.Tensor:
+        """[H] float32: largest value scale written to each head since the reset."""
+        lay = self.layout(layer)
+        return self._view(lay.vmax, 4 * self.n_heads, torch.float32)
 
     def slot_pos(self, layer: int) -> torch.Tensor:
         lay = self.layout(layer)

@@ -26,14 +26,24 @@ int hip_fail(hipError_t e, const char* what) {
 
 constexpr size_t kAlign = 256;
 constexpr size_t kConstsBytes = 4096;
-constexpr int kMaxSplits = 8;
+constexpr int kMaxWorkgroups = 4096;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Compute units of the current device (the persistent attention grid has one
+// workgroup per unit); 256 on MI355X.
+int compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    return n;
+  return 256;
+}
 
 struct Plan {
   rkv::Geom g;
   rkv::AttnWs ws;  // pointers filled relative to base 0 (offsets) until create
-  size_t ws_qcodes, ws_qscale, ws_headc, ws_parto, ws_partml;
+  size_t ws_parto, ws_partml, ws_count;
   size_t total;
 };
 
@@ -51,6 +61,8 @@ bool params_ok(const rkv_params* p, std::string* why) {
     return *why = "rope_base must be finite and > 1", false;
   if (!(p->scale_margin > 0.0f) || !(p->scale_margin <= 64.0f))
     return *why = "scale_margin must be in (0, 64]", false;
+  if (p->attn_workgroups < 0 || p->attn_workgroups > kMaxWorkgroups)
+    return *why = "attn_workgroups out of range [0, 4096]", false;
   return true;
 }
 
@@ -81,28 +93,26 @@ Plan make_plan(const rkv_params* p) {
   o = align_up(o + NP * 4, kAlign);
   g.off_state = o;
   o = align_up(o + 16, kAlign);
+  g.off_vmax = o;
+  o = align_up(o + H * 4, kAlign);
   g.layer_bytes = o;
 
   size_t w = g.layer0 + (size_t)p->n_layers * g.layer_bytes;
-  const size_t nq_pad = align_up((size_t)p->max_queries, 32);
-  const size_t nqb = nq_pad / 32;
-  int splits = (int)((2 * 256 + nqb * H - 1) / (nqb * H));
-  if (splits < 1) splits = 1;
-  if (splits > kMaxSplits) splits = kMaxSplits;
-  pl.ws.nq_pad = (int32_t)nq_pad;
-  pl.ws.splits = splits;
+  // Attention workspace: one partial result (32 query rows) per segment of
+  // the persistent grid -- at most units + workgroups of them -- and one
+  // arrival counter per unit.
+  const size_t nqb = align_up((size_t)p->max_queries, 32) / 32;
+  const size_t units = nqb * H;
+  const int grid = p->attn_workgroups > 0 ? p->attn_workgroups : compute_units();
+  const size_t segs = units + (size_t)grid;
+  pl.ws.grid = grid;
   pl.ws.terms = p->precision == RKV_PRECISE ? 2 : 1;
-  pl.ws_qcodes = w;
-  w = align_up(w + 2 * H * nq_pad * D, kAlign);
-  pl.ws_qscale = w;
-  w = align_up(w + 2 * H * nq_pad, kAlign);
-  pl.ws_headc = w;
-  w = align_up(w + H * 4, kAlign);
-  const size_t units = nqb * H * (size_t)splits;
   pl.ws_parto = w;
-  w = align_up(w + units * 32 * D * 4, kAlign);
+  w = align_up(w + segs * 32 * D * 4, kAlign);
   pl.ws_partml = w;
-  w = align_up(w + units * 32 * 2 * 4, kAlign);
+  w = align_up(w + segs * 32 * 2 * 4, kAlign);
+  pl.ws_count = w;
+  w = align_up(w + units * 4, kAlign);
   pl.total = w;
   return pl;
 }
@@ -150,11 +160,9 @@ int ring_cache_create(const rkv_params* p, void* dev_buf, size_t bytes, hipStrea
   c->g = pl.g;
   c->g.base = static_cast<uint8_t*>(dev_buf);
   c->ws = pl.ws;
-  c->ws.qcodes = c->g.base + pl.ws_qcodes;
-  c->ws.qscale = c->g.base + pl.ws_qscale;
-  c->ws.head_c = reinterpret_cast<float*>(c->g.base + pl.ws_headc);
   c->ws.part_o = reinterpret_cast<float*>(c->g.base + pl.ws_parto);
   c->ws.part_ml = reinterpret_cast<float*>(c->g.base + pl.ws_partml);
+  c->ws.count = reinterpret_cast<int32_t*>(c->g.base + pl.ws_count);
   c->bytes = pl.total;
   const int half = p->head_dim / 2;
   for (int j = 0; j < half; ++j) {
@@ -215,6 +223,7 @@ int ring_cache_layout(const rkv_cache* c, int32_t layer, rkv_layout* out) {
   out->scale_v = b + c->g.off_scale_v;
   out->slot_pos = b + c->g.off_slot_pos;
   out->state = b + c->g.off_state;
+  out->vmax = b + c->g.off_vmax;
   out->layer_bytes = c->g.layer_bytes;
   out->n_slots_padded = c->g.n_pad;
   return RKV_OK;

@@ -11,14 +11,11 @@ namespace rkv {
 
 // Attention workspace inside the cache buffer (shared by all layers).
 struct AttnWs {
-  uint8_t* qcodes;   // [terms][H][nq_pad][D] e4m3 query codes
-  uint8_t* qscale;   // [terms][H][nq_pad] E8M0 scale bytes (127 + exponent)
-  float* head_c;     // [H] probability scale c_h = 448 * 2^-headroom / max s_v
-  float* part_o;     // [units][32][D] fp32 partial outputs (split-KV)
-  float* part_ml;    // [units][32][2] fp32 partial (max, sum)
-  int32_t nq_pad;    // query rows allocated per head (multiple of 32)
-  int32_t splits;    // KV splits per (head, 32-query block)
-  int32_t terms;     // 2 = precise, 1 = fast
+  float* part_o;   // [units + grid][32][D] fp32 partial outputs of split units
+  float* part_ml;  // [units + grid][32][2] fp32 partial (running max, sum)
+  int32_t* count;  // [units] arrival counters of split units (zero between calls)
+  int32_t grid;    // persistent workgroups
+  int32_t terms;   // 2 = precise, 1 = fast
 };
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);

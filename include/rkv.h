@@ -69,6 +69,8 @@ typedef struct {
   int32_t precision;   /* RKV_PRECISE or RKV_FAST */
   float rope_base;     /* RoPE base, omega_j = base^(-2j/D); 10000 */
   float scale_margin;  /* scale s = margin * amax / 448; 1.0 */
+  int32_t attn_workgroups; /* persistent workgroups of one attention call
+                              (1 .. 4096); 0 = one per compute unit */
 } rkv_params;
 
 /* Byte offsets into the cache buffer for one layer.  Layout (N_pad = N
@@ -83,9 +85,12 @@ typedef struct {
  *   state    i32 [4]                  {head, n_valid, ticket, 0}: the next
  *                                      write slot, the number of valid slots
  *                                      (the cyclic range [head-n_valid, head)),
- *                                      and a kernel-internal counter. */
+ *                                      and a kernel-internal counter.
+ *   vmax     f32 [H]                  per head, the largest value scale
+ *                                      written since the last reset (an upper
+ *                                      bound of every cached value scale). */
 typedef struct {
-  size_t codes_k, codes_v, scale_k, scale_v, slot_pos, state;
+  size_t codes_k, codes_v, scale_k, scale_v, slot_pos, state, vmax;
   size_t layer_bytes; /* distance between consecutive layers */
   int32_t n_slots_padded;
 } rkv_layout;
@@ -107,7 +112,7 @@ int ring_cache_create(const rkv_params* p, void* dev_buf, size_t bytes, hipStrea
 int ring_cache_destroy(rkv_cache* c);
 
 /* Session reset (§6 "Session start" clears the dynamic cache): set head,
- * n_valid and every slot position of one layer (or all layers when
+ * n_valid, vmax and every slot position of one layer (or all layers when
  * layer == -1) to zero.  Codes and scales are left as they are; slots
  * outside the valid range are never read. */
 int ring_cache_reset(rkv_cache* c, int32_t layer, hipStream_t stream);

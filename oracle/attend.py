@@ -27,12 +27,15 @@ The device kernel's declared numerics, which ``attend_method`` and
   r = q - decode(codes) * 2**e is quantized the same way and the kernel
   multiplies K by both terms; Q is then known to about 2**-8 relative.
 * P.V in FP8: with P = exp(S - m) (m the row maximum), the kernel feeds
-  x = P * s_v[j] * c with c = 448 * 2**-headroom / max_j s_v[j] over the
-  head's valid slots, as hi = e4m3(x) and, with two terms, as
+  x = P * s_v[j] * c with c = 448 * 2**-headroom / vmax_h, vmax_h the largest
+  value scale written to the head since the last reset (an upper bound of
+  every cached s_v), as hi = e4m3(x) and, with two terms, as
   lo = e4m3(16 (x - hi)) / 16; it multiplies them by the V codes and divides
-  by c * sum_j P.  ``attend_emul`` uses the final row maximum; the kernel's
-  running maximum changes which way some codes round, which the tolerance
-  covers.
+  by c * sum_j P.  The kernel keeps a running row maximum that it raises only
+  when a tile exceeds it by more than 2 in log2 units, so its P may reach 4:
+  headroom 2 keeps x <= 448.  ``attend_emul`` uses the final row maximum; the
+  kernel's running maximum changes which way some codes round, which the
+  tolerance covers.
 * The single-term ("fast") mode drops both residual terms.
 """
 from __future__ import annotations
@@ -131,7 +134,7 @@ def attend_method(st: RingState, q: np.ndarray, q_pos: np.ndarray, q_terms: int 
 
 
 def attend_emul(st: RingState, q: np.ndarray, q_pos: np.ndarray, q_terms: int = 2,
-                p_terms: int = 2, headroom: int = 0) -> np.ndarray:
+                p_terms: int = 2, headroom: int = 2) -> np.ndarray:
     """A-emul: A-method plus the FP8 rounding of P' = P * s_v[j] * c (see module doc)."""
     qr, slots = _prepare(st, q, q_pos)
     out = np.zeros(qr.shape, dtype=np.float64)
@@ -146,7 +149,7 @@ def attend_emul(st: RingState, q: np.ndarray, q_pos: np.ndarray, q_terms: int = 
         s = qd[:, h, :] @ kd[h].T / math.sqrt(d)
         p = np.exp(s - s.max(axis=1, keepdims=True))  # <= 1, row max exactly 1
         l = p.sum(axis=1, keepdims=True)
-        smax = sv[h].max()
+        smax = st.vmax[h]
         c = (e4m3.E4M3_MAX * 2.0 ** (-headroom) / smax) if smax > 0 else 1.0
         c = float(np.float32(c))
         pq = p_terms_value(p * sv[h][None, :] * c, p_terms)

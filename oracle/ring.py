@@ -25,7 +25,10 @@ statement (each is listed in DESIGN.md):
   slots are rotated and their positions shifted.
 
 State layout (canonical, independent of any device layout): codes [H][N][D]
-uint8, scales [H][N] float64 holding fp32 values, slot_pos [N] int64.
+uint8, scales [H][N] float64 holding fp32 values, slot_pos [N] int64, and
+vmax [H], the largest value scale written to each head since the last reset
+(bookkeeping the device kernels keep so the attention knows an upper bound of
+every cached value scale without a pass over the cache).
 """
 from __future__ import annotations
 
@@ -51,6 +54,7 @@ class RingState:
     codes_v: np.ndarray = field(default=None)
     scale_k: np.ndarray = field(default=None)
     scale_v: np.ndarray = field(default=None)
+    vmax: np.ndarray = field(default=None)  # per head: largest s_v written since the reset
 
     def __post_init__(self):
         n, h, d = self.n_slots, self.n_heads, self.head_dim
@@ -64,11 +68,14 @@ class RingState:
             self.scale_k = np.zeros((h, n), dtype=np.float64)
         if self.scale_v is None:
             self.scale_v = np.zeros((h, n), dtype=np.float64)
+        if self.vmax is None:
+            self.vmax = np.zeros(h, dtype=np.float64)
 
     def copy(self) -> "RingState":
         return RingState(self.n_slots, self.n_heads, self.head_dim, self.rope_base, self.margin,
                          self.head, self.n_valid, self.slot_pos.copy(), self.codes_k.copy(),
-                         self.codes_v.copy(), self.scale_k.copy(), self.scale_v.copy())
+                         self.codes_v.copy(), self.scale_k.copy(), self.scale_v.copy(),
+                         self.vmax.copy())
 
 
 def valid_slots(st: RingState) -> np.ndarray:
@@ -106,6 +113,7 @@ def write(st: RingState, k: np.ndarray, v: np.ndarray, pos: np.ndarray) -> None:
     st.scale_k[:, slots] = sk.T
     st.scale_v[:, slots] = sv.T
     st.slot_pos[slots] = pos
+    st.vmax = np.maximum(st.vmax, sv.max(axis=0))
     st.head = int((st.head + n) % st.n_slots)
     st.n_valid = int(min(st.n_valid + n, st.n_slots))
 
@@ -130,10 +138,11 @@ def rotate(st: RingState, delta: int) -> None:
 
 
 def reset(st: RingState) -> None:
-    """Session reset: empty ring (head 0, no valid slots, positions 0)."""
+    """Session reset: empty ring (head 0, no valid slots, positions 0, vmax 0)."""
     st.head = 0
     st.n_valid = 0
     st.slot_pos[:] = 0
+    st.vmax[:] = 0
 
 
 def dequant_k(st: RingState) -> np.ndarray:

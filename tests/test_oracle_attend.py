@@ -96,9 +96,10 @@ def test_one_valid_slot_returns_its_value():
     for fn in (attend.attend_exact, attend.attend_method):
         out = fn(st, q, np.arange(7))
         assert np.max(np.abs(out - vd[None])) < 1e-15, fn.__name__
-    # emul: P' = 1 * s_v * c = 448 exactly up to the fp32 rounding of c
-    out = attend.attend_emul(st, q, np.arange(7))
-    assert np.all(np.abs(out - vd[None]) <= 2 ** -22 * np.abs(vd[None]))
+    # emul: P' = 1 * s_v * c = 448 * 2**-headroom exactly up to the fp32 rounding of c
+    for hr in (0, 2):
+        out = attend.attend_emul(st, q, np.arange(7), headroom=hr)
+        assert np.all(np.abs(out - vd[None]) <= 2 ** -22 * np.abs(vd[None]))
 
 
 def test_identical_keys_give_mean_of_values():
@@ -201,6 +202,21 @@ def test_round_bf16_closed_forms_and_torch():
     x32 = (rng.standard_normal(100_000) * 10).astype(np.float32)
     ref = torch.tensor(x32).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(round_bf16(x32.astype(np.float64)), ref)
+
+
+def test_vmax_tracks_largest_value_scale_since_reset():
+    rng = np.random.default_rng(14)
+    st = ring.RingState(20, 2, 8)
+    big = rng.standard_normal((5, 2, 8)) * 100
+    ring.write(st, rng.standard_normal((5, 2, 8)), big, np.arange(5))
+    first = st.vmax.copy()
+    assert np.allclose(first, st.scale_v[:, :5].max(axis=1))
+    for c in range(6):  # overwrite the ring with small values: vmax stays an upper bound
+        ring.write(st, rng.standard_normal((10, 2, 8)), rng.standard_normal((10, 2, 8)), np.arange(10))
+    assert np.array_equal(st.vmax, first)
+    assert np.all(st.vmax >= st.scale_v.max(axis=1))
+    ring.reset(st)
+    assert not st.vmax.any()
 
 
 def test_sigma_v_shape_and_value():
