@@ -26,6 +26,9 @@ FLAGS = [
     "-Wall",
     # packed fp32 ALU ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no value here is ever NaN: min/max need no quieting of their inputs
+    # (infinities keep their meaning: -inf marks masked slots)
+    "-fno-honor-nans",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

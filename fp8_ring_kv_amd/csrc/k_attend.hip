@@ -6,33 +6,34 @@
 // used as stored (§4.2); the cache is e4m3 with per-head descales and only
 // the queries are quantized per call (§4.3).
 //
-// Work: unit u = (head h, block qb of 32 queries), u = h * nqb + qb; each
+// Work: unit u = (head h, group qg of 128 queries), u = h * nqg + qg; each
 // unit needs `count` 64-slot tiles (the tiles holding valid slots, in cyclic
 // order from the tile of the oldest valid slot).  A persistent grid of G
-// workgroups (one per compute unit) cuts the unit-major list of all
+// workgroups (two per compute unit) cuts the unit-major list of all
 // units * count (unit, tile) pairs into G equal contiguous ranges, so every
 // workgroup gets the same matrix work to within one tile.  Workgroups are
 // dealt to the 8 XCDs round-robin; ranges are assigned so that each XCD
-// takes a contiguous block of them (a few heads), keeping their K/V in its L2.
+// takes a contiguous block of them (one or two heads), keeping their K/V in
+// its L2.
 //
 // A workgroup handles each unit its range meets as one segment:
-//   1. RoPE on the unit's 32 queries (angles in double precision) and their
+//   1. RoPE on the unit's 128 queries (angles in double precision) and their
 //      split into one or two e4m3 terms with power-of-two scales (applied
 //      exactly by the E8M0 scale operand of the matrix instruction), staged
-//      in LDS;
-//   2. its 4 waves take interleaved tiles of the segment.  Per tile a wave
-//      computes S^T = K Q^T with v_mfma_scale_f32_32x32x64_f8f6f4 (rows =
-//      slots, columns = queries: one lane owns one query, so the row max and
-//      sum are in-lane plus one swap with lane ^ 32), applies the per-slot
-//      key scale, updates an online softmax in fp32 (exp2 domain), turns
+//      in LDS; wave w keeps queries 32 w .. 32 w + 31 in registers;
+//   2. the tiles stream through two LDS buffers: the K tile, the transposed
+//      V tile and the 128 slot scales of tile i + 1 are copied from global
+//      memory straight into LDS (global_load_lds_dwordx4) while tile i is
+//      computed.  All 4 waves read each tile.  Per tile a wave computes
+//      S^T = K Q^T with v_mfma_scale_f32_32x32x64_f8f6f4 (rows = slots,
+//      columns = queries: one lane owns one query, so the row max and sum
+//      are in-lane plus one swap with lane ^ 32), applies the per-slot key
+//      scale, updates an online softmax in fp32 (exp2 domain), turns
 //      P * s_v * c_h into one or two e4m3 terms and accumulates
-//      O^T += V^T P^T with the same instruction.  The loop is software
-//      pipelined: the next tile's Q K^T products are issued before this
-//      tile's softmax, so the matrix cores and the vector ALUs overlap;
-//   3. the 4 waves merge in LDS;
-//   4. a whole unit writes its bf16 output; a unit split between
-//      workgroups writes a partial (O, max, sum) and the last workgroup to
-//      finish its part merges the partials and writes the output.
+//      O^T += V^T P^T with the same instruction;
+//   3. a whole unit writes its bf16 output; a unit split between
+//      workgroups writes a partial (O, max, sum) per wave and the last
+//      workgroup to finish its part merges the partials.
 //
 // Probability scale: c_h = 448 / (4 vmax_h), vmax_h being the largest value
 // scale written to head h since the reset (kept by the write kernel).  The
@@ -44,16 +45,20 @@ namespace rkv {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;  // LDS byte, addressed without a generic pointer
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 2.f;  // log2 headroom of the running maximum
+constexpr int kQG = 128;      // queries per unit: 4 waves x 32
 
 struct AttnArgs {
   Geom g;
   AttnWs ws;
   int layer;
   int n_q;
-  int nqb;  // 32-query blocks
+  int nqg;  // 128-query groups
   const uint4* q;
   const int32_t* q_pos;
   uint16_t* out;
@@ -74,33 +79,24 @@ __device__ inline int pow2_exponent(float amax) {
 __device__ inline float bcast16(float v, int r) {
   int x = __float_as_int(v);
   switch (r) {
-    case 0: x = __builtin_amdgcn_update_dpp(0, x, 0x150, 0xF, 0xF, false); break;
-    case 1: x = __builtin_amdgcn_update_dpp(0, x, 0x151, 0xF, 0xF, false); break;
-    case 2: x = __builtin_amdgcn_update_dpp(0, x, 0x152, 0xF, 0xF, false); break;
-    case 3: x = __builtin_amdgcn_update_dpp(0, x, 0x153, 0xF, 0xF, false); break;
-    case 4: x = __builtin_amdgcn_update_dpp(0, x, 0x154, 0xF, 0xF, false); break;
-    case 5: x = __builtin_amdgcn_update_dpp(0, x, 0x155, 0xF, 0xF, false); break;
-    case 6: x = __builtin_amdgcn_update_dpp(0, x, 0x156, 0xF, 0xF, false); break;
-    case 7: x = __builtin_amdgcn_update_dpp(0, x, 0x157, 0xF, 0xF, false); break;
-    case 8: x = __builtin_amdgcn_update_dpp(0, x, 0x158, 0xF, 0xF, false); break;
-    case 9: x = __builtin_amdgcn_update_dpp(0, x, 0x159, 0xF, 0xF, false); break;
-    case 10: x = __builtin_amdgcn_update_dpp(0, x, 0x15A, 0xF, 0xF, false); break;
-    case 11: x = __builtin_amdgcn_update_dpp(0, x, 0x15B, 0xF, 0xF, false); break;
-    case 12: x = __builtin_amdgcn_update_dpp(0, x, 0x15C, 0xF, 0xF, false); break;
-    case 13: x = __builtin_amdgcn_update_dpp(0, x, 0x15D, 0xF, 0xF, false); break;
-    case 14: x = __builtin_amdgcn_update_dpp(0, x, 0x15E, 0xF, 0xF, false); break;
-    case 15: x = __builtin_amdgcn_update_dpp(0, x, 0x15F, 0xF, 0xF, false); break;
+    case 0: x = __builtin_amdgcn_mov_dpp(x, 0x150, 0xF, 0xF, true); break;
+    case 1: x = __builtin_amdgcn_mov_dpp(x, 0x151, 0xF, 0xF, true); break;
+    case 2: x = __builtin_amdgcn_mov_dpp(x, 0x152, 0xF, 0xF, true); break;
+    case 3: x = __builtin_amdgcn_mov_dpp(x, 0x153, 0xF, 0xF, true); break;
+    case 4: x = __builtin_amdgcn_mov_dpp(x, 0x154, 0xF, 0xF, true); break;
+    case 5: x = __builtin_amdgcn_mov_dpp(x, 0x155, 0xF, 0xF, true); break;
+    case 6: x = __builtin_amdgcn_mov_dpp(x, 0x156, 0xF, 0xF, true); break;
+    case 7: x = __builtin_amdgcn_mov_dpp(x, 0x157, 0xF, 0xF, true); break;
+    case 8: x = __builtin_amdgcn_mov_dpp(x, 0x158, 0xF, 0xF, true); break;
+    case 9: x = __builtin_amdgcn_mov_dpp(x, 0x159, 0xF, 0xF, true); break;
+    case 10: x = __builtin_amdgcn_mov_dpp(x, 0x15A, 0xF, 0xF, true); break;
+    case 11: x = __builtin_amdgcn_mov_dpp(x, 0x15B, 0xF, 0xF, true); break;
+    case 12: x = __builtin_amdgcn_mov_dpp(x, 0x15C, 0xF, 0xF, true); break;
+    case 13: x = __builtin_amdgcn_mov_dpp(x, 0x15D, 0xF, 0xF, true); break;
+    case 14: x = __builtin_amdgcn_mov_dpp(x, 0x15E, 0xF, 0xF, true); break;
+    case 15: x = __builtin_amdgcn_mov_dpp(x, 0x15F, 0xF, 0xF, true); break;
   }
   return __int_as_float(x);
-}
-
-__device__ inline v8i load32(const uint8_t* p0, const uint8_t* p1) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p0);
-  const uint4 b = *reinterpret_cast<const uint4*>(p1);
-  v8i r;
-  r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
-  r[4] = (int)b.x; r[5] = (int)b.y; r[6] = (int)b.z; r[7] = (int)b.w;
-  return r;
 }
 
 __device__ inline v16f mfma_fp8(v8i a, v8i b, v16f c, int sa, int sb) {
@@ -118,6 +114,92 @@ __device__ inline float half_swap_add(float x) {
 }
 
 // ---------------------------------------------------------------------------
+// One tile in LDS, filled by wave-wide copies of 16 bytes per lane (1 KiB
+// chunks): D/16 chunks of K, D/16 chunks of transposed V, then the scales.
+//   K: 16-byte piece c of slot row r sits at piece r * (D/16) + (c ^ ksw(r)).
+//      A wave reads its K operand as lane li -> row krow(li) (below); the
+//      swizzle puts the 8 rows read by every 8 consecutive lanes on 8
+//      different 16-byte bank groups.
+//   V^T: piece c (0..3) of row d at piece 4 d + (c ^ ((d >> 1) & 3)); 8
+//      consecutive lanes read 8 consecutive rows, again on distinct groups.
+//   scales: s_k[64] at byte 0, s_v[64] at byte 256 of the scale area.
+template <int D>
+struct TileLds {
+  static constexpr int KC = D / 16;  // K chunks (= V chunks)
+  static constexpr int V_OFF = KC * 1024;
+  static constexpr int S_OFF = 2 * KC * 1024;
+  static constexpr int BYTES = 2 * KC * 1024 + 512;
+  static constexpr int COPIES = KC / 2 + 1;  // copy instructions per wave and tile
+};
+
+constexpr int kBufs = 6;   // tile buffers: three pairs (one tile per wave group)
+constexpr int kPairs = kBufs / 2;
+
+template <int D>
+__device__ inline int ksw(int r) {
+  return D == 128 ? ((r & 3) | (((r >> 4) & 1) << 2)) : (((r >> 1) & 1) | (((r >> 4) & 1) << 1));
+}
+__device__ inline int vsw(int d) { return (d >> 1) & 3; }
+
+struct TileSrc {
+  const uint8_t* kbase;  // codes_k of the head
+  const uint8_t* vbase;  // codes_v of the head
+  const float* skb;      // scale_k of the head
+  const float* svb;      // scale_v of the head
+};
+
+// Per-lane source offsets of one wave's copies.  Wave w copies K chunks
+// w, w + 4, .. (chunk c holds pieces P = 64 c + lane: row r = P / (D/16),
+// stored piece P % (D/16)), the V chunks with the same numbers, and a quarter
+// of the scales.  With the swizzle, the source column of a K piece depends on
+// the lane and on one bit of c (bit 1 for D = 128, bit 0 for D = 64) that is
+// the same for all of a wave's chunks, so one offset (relative to the chunk's
+// first row) serves them all; V likewise.
+template <int D>
+struct CopyOffsets {
+  uint32_t k, v;
+  __device__ CopyOffsets(int wave, int lane) {
+    constexpr int PR = D / 16;  // pieces per K row
+    const int P = wave * 64 + lane, r = P / PR, lc = (P % PR) ^ ksw<D>(r);
+    k = (uint32_t)((r - wave * (64 / PR)) * D + 16 * lc);
+    const int d = lane >> 2;  // row within a V chunk (16 rows of 64 bytes)
+    v = (uint32_t)(64 * d + 16 * ((lane & 3) ^ vsw(d)));
+  }
+};
+
+__device__ inline void copy16(const void* gp, lds_u8* lp) {
+  __builtin_amdgcn_global_load_lds((global_void*)gp, (lds_void*)lp, 16, 0, 0);
+}
+
+// Copy tile T of the head into an LDS buffer (this wave's share: the same
+// number of copy instructions in every wave, TileLds::COPIES).
+template <int D>
+__device__ inline void copy_tile(lds_u8* lbuf, const TileSrc& src, int T, const CopyOffsets<D>& co,
+                                 int wave, int lane) {
+  constexpr int KC = TileLds<D>::KC;
+  const uint8_t* kt = src.kbase + (size_t)T * kTile * D;
+  const uint8_t* vt = src.vbase + (size_t)T * kTile * D;
+#pragma unroll
+  for (int j = 0; j < KC / 4; ++j) {
+    const int c = wave + 4 * j;
+    copy16(kt + c * 1024 + co.k, lbuf + c * 1024);
+    copy16(vt + c * 1024 + co.v, lbuf + TileLds<D>::V_OFF + c * 1024);
+  }
+  // scales: waves 0, 1 copy s_k[32 w, +32), waves 2, 3 s_v[32 (w - 2), +32),
+  // 4 per lane on lanes 0..7
+  const float* sb = (wave < 2 ? src.skb : src.svb) + T * kTile + 32 * (wave & 1);
+  if (lane < 8) copy16(sb + 4 * lane, lbuf + TileLds<D>::S_OFF + 128 * wave);
+}
+
+// Wait until at most N of this wave's vector memory operations are in flight
+// (the copies of the tiles after the one needed), then meet the other waves:
+// after the barrier every wave's copies of that tile have landed.  One asm
+// block, so no LDS access moves across it.
+template <int N>
+__device__ inline void wait_copies_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // Per-wave tile operands (lane = li + 32 gq).
 //   K operand of S^T = K Q^T: lane li holds slot 32 sub + krow(li), bytes
 //   [64 ks + 32 gq, +32).  krow permutes the slots so that accumulator
@@ -136,39 +218,58 @@ struct VOp {
   float sk[2], sv[2];
 };
 
-struct TileSrc {
-  const uint8_t* kbase;  // codes_k of the head
-  const uint8_t* vbase;  // codes_v of the head
-  const float* skb;      // scale_k of the head
-  const float* svb;      // scale_v of the head
+__device__ inline v8i lds32(const lds_u8* p0, const lds_u8* p1) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) const u32x4 lds_u4;
+  const u32x4 a = *reinterpret_cast<lds_u4*>(p0);
+  const u32x4 b = *reinterpret_cast<lds_u4*>(p1);
+  v8i r;
+  r[0] = (int)a[0]; r[1] = (int)a[1]; r[2] = (int)a[2]; r[3] = (int)a[3];
+  r[4] = (int)b[0]; r[5] = (int)b[1]; r[6] = (int)b[2]; r[7] = (int)b[3];
+  return r;
+}
+
+// Per-lane byte offsets of the operand pieces inside a tile buffer.  With
+// the swizzles the lane-dependent part of every K piece is one of 2 KS values
+// (the half h and block ks enter by XOR) and the slot half sub by a constant;
+// V pieces by XOR of the half h and a constant per 32-row block.
+template <int D>
+struct TileOffsets {
+  uint32_t k[D / 64][2];
+  uint32_t v[2];
+  uint32_t s;
+  __device__ TileOffsets(int lane) {
+    const int li = lane & 31, gq = lane >> 5;
+    const int krow = 16 * ((li >> 2) & 1) + 4 * (li >> 3) + (li & 3);
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) k[ks][h] = (uint32_t)(krow * D + 16 * ((4 * ks + 2 * gq + h) ^ ksw<D>(krow)));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) v[h] = (uint32_t)(TileLds<D>::V_OFF + 64 * li + 16 * ((gq + 2 * h) ^ vsw(li)));
+    s = (uint32_t)(TileLds<D>::S_OFF + 4 * (16 * gq + (lane & 15)));
+  }
 };
 
 template <int D>
-__device__ inline void load_k(KOp<D>& f, const TileSrc& src, int T, int lane) {
-  const int li = lane & 31, gq = lane >> 5;
-  const int krow = 16 * ((li >> 2) & 1) + 4 * (li >> 3) + (li & 3);
+__device__ inline void read_k(KOp<D>& f, const lds_u8* lb, const TileOffsets<D>& o) {
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    const uint8_t* kp = src.kbase + (size_t)(T * kTile + 32 * sub + krow) * D + 32 * gq;
+  for (int sub = 0; sub < 2; ++sub)  // slot half sub: rows + 32, a constant offset (ksw ignores bit 5)
 #pragma unroll
-    for (int ks = 0; ks < D / 64; ++ks) f.k[sub][ks] = load32(kp + 64 * ks, kp + 64 * ks + 16);
-  }
+    for (int ks = 0; ks < D / 64; ++ks)
+      f.k[sub][ks] = lds32(lb + 32 * D * sub + o.k[ks][0], lb + 32 * D * sub + o.k[ks][1]);
 }
 
 template <int D>
-__device__ inline void load_v(VOp<D>& f, const TileSrc& src, int T, int lane) {
-  const int li = lane & 31, gq = lane >> 5;
-  const uint8_t* vt = src.vbase + (size_t)T * D * kTile;
+__device__ inline void read_v(VOp<D>& f, const lds_u8* lb, const TileOffsets<D>& o) {
 #pragma unroll
-  for (int b = 0; b < D / 32; ++b) {
-    const uint8_t* vp = vt + (size_t)(32 * b + li) * kTile + 16 * gq;
-    f.v[b] = load32(vp, vp + 32);
-  }
+  for (int b = 0; b < D / 32; ++b)  // row block b: rows + 32 b, a constant offset (vsw ignores bit 5)
+    f.v[b] = lds32(lb + 2048 * b + o.v[0], lb + 2048 * b + o.v[1]);
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
-    const int cs = T * kTile + 32 * sub + 16 * gq + (lane & 15);
-    f.sk[sub] = src.skb[cs];
-    f.sv[sub] = src.svb[cs];
+    typedef __attribute__((address_space(3))) const float lds_f;
+    f.sk[sub] = *reinterpret_cast<lds_f*>(lb + o.s + 128 * sub);
+    f.sv[sub] = *reinterpret_cast<lds_f*>(lb + o.s + 256 + 128 * sub);
   }
 }
 
@@ -195,6 +296,9 @@ struct WaveState {
 template <int D, int TERMS>
 __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>& st,
                                   unsigned long long mask, float kscale, float ch, int lane) {
+  // x = P s_v c_h is formed once and reused; contracting x - e4m3(x) into
+  // fma(P, s_v c_h, -e4m3(x)) would keep the broadcast scale in a register
+#pragma clang fp contract(off)
   constexpr int DB = D / 32;
   const int gq = lane >> 5;
   const float tk0 = vf.sk[0] * kscale, tk1 = vf.sk[1] * kscale;
@@ -205,11 +309,13 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
     acc[1][r] *= bcast16(tk1, r);
   }
   if (mask != ~0ull) {  // partially valid tile (ring edge, partial fill, padding)
+    const uint32_t m0 = (uint32_t)(mask >> (16 * gq)) & 0xFFFFu;  // slots 16 gq + r
+    const uint32_t m1 = (uint32_t)(mask >> (32 + 16 * gq)) & 0xFFFFu;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (!((mask >> (32 * sub + 16 * gq + r)) & 1ull)) acc[sub][r] = -INFINITY;
+    for (int r = 0; r < 16; ++r) {
+      if (!((m0 >> r) & 1u)) acc[0][r] = -INFINITY;
+      if (!((m1 >> r) & 1u)) acc[1][r] = -INFINITY;
+    }
   }
   float tmax = -INFINITY;
 #pragma unroll
@@ -225,6 +331,10 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
   }
   // P <= 4 and s_v c_h <= 112, so the conversions below never overflow
   // (fp32 rounding a hair above 448 still rounds to 448 in e4m3).
+  // The empty asm keeps the value-scale broadcasts below the branch above,
+  // next to their multiplies, which then take them as a DPP operand.
+  float svx0 = sv0, svx1 = sv1;
+  asm volatile("" : "+v"(svx0), "+v"(svx1));
   v8i ph, pl;
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
@@ -234,7 +344,7 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
     for (int e = 0; e < 4; ++e) {
       const float p = __builtin_amdgcn_exp2f(acc[sub][r0 + e] - st.m);
       st.l += p;
-      x[e] = p * bcast16(sub ? sv1 : sv0, r0 + e);
+      x[e] = p * bcast16(sub ? svx1 : svx0, r0 + e);
     }
     uint32_t hw = pack2_fp8<false>(x[0], x[1], 0u);
     hw = pack2_fp8<true>(x[2], x[3], hw);
@@ -254,43 +364,107 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
   }
 }
 
+
 template <int D>
 struct __attribute__((aligned(16))) AttnSmem {
-  uint8_t q[2][32 * (D + 16)];  // staged query codes per term, rows padded by 16 bytes
-  int qexp[2][32];
-  float merge[4][32 * D + 64];  // per wave: O^T as [d][32 queries], then m[32], l[32]
+  uint8_t kv[kBufs][TileLds<D>::BYTES];  // ring of tile buffers
   int flag;
 };
 
-// bf16 output row piece: n = D / 8 columns of one query row
-template <int CPT>
-__device__ inline void store_out(uint16_t* dst, const float (&o)[CPT], float inv) {
-  uint32_t pk[CPT / 2];
+// ---------------------------------------------------------------------------
+// Query preparation, one launch before the attention: RoPE at q_pos (angles
+// in double precision) and the split of each (query, head) row into TERMS
+// e4m3 terms with power-of-two scales: term t holds e4m3(y_t / 2^e_t) with
+// e_t the smallest exponent that fits the row (448 * 2^e_t >= amax), y_0 = y
+// and y_{t+1} the residual; the E8M0 operand 127 + e_t of the matrix
+// instruction applies 2^e_t exactly.  Rows n_q .. nq_rows - 1 are zero.
+// One lane per RoPE pair; D/2 lanes per row.
+struct QPrepArgs {
+  Geom g;
+  AttnWs ws;
+  int n_q;
+  int nq_rows;  // 128-query groups of this call x 128
+  const uint32_t* q;  // bf16 pairs [n_q][H][D/2]
+  const int32_t* q_pos;
+};
+
+template <int D, int TERMS>
+__global__ __launch_bounds__(256) void q_prep_kernel(QPrepArgs A) {
+  constexpr int LPR = D / 2;     // lanes per row
+  constexpr int RPW = 64 / LPR;  // rows per wave
+  const int H = A.g.n_heads;
+  const int lane = threadIdx.x & 63;
+  const int r = (int)((blockIdx.x * 256 + threadIdx.x) >> 6) * RPW + lane / LPR;  // h * nq_rows + qi
+  if (r >= H * A.nq_rows) return;  // whole rows only: the reductions stay inside live lanes
+  const int j = lane % LPR;
+  const int h = r / A.nq_rows, qi = r % A.nq_rows;
+  float y0 = 0.f, y1 = 0.f;
+  if (qi < A.n_q) {
+    const uint32_t w = A.q[((size_t)qi * H + h) * (D / 2) + j];
+    float cs, sn;
+    rope_cs(A.q_pos[qi], omega_turns(A.g)[j], cs, sn);
+    const float x0 = bf16_lo(w), x1 = bf16_hi(w);
+    y0 = x0 * cs - x1 * sn;
+    y1 = x0 * sn + x1 * cs;
+  }
+  float am = fmaxf(fabsf(y0), fabsf(y1));
 #pragma unroll
-  for (int c = 0; c < CPT / 2; ++c)
-    pk[c] = f32_to_bf16_rne(o[2 * c] * inv) | (f32_to_bf16_rne(o[2 * c + 1] * inv) << 16);
+  for (int t = 0; t < TERMS; ++t) {
+    am = group_max<LPR>(am);
+    const int e = am > 0.f ? pow2_exponent(am) : 0;
+    const uint32_t cw = pack2_fp8<false>(clamp448(ldexpf(y0, -e)), clamp448(ldexpf(y1, -e)), 0u);
+    const size_t row = ((size_t)t * H + h) * A.ws.nq_pad + qi;
+    reinterpret_cast<uint16_t*>(A.ws.qcodes + row * D)[j] = (uint16_t)cw;
+    if (j == 0) A.ws.qexp[row] = e;
+    float d0, d1, d2, d3;
+    unpack4_fp8(cw, d0, d1, d2, d3);
+    y0 -= ldexpf(d0, e);
+    y1 -= ldexpf(d1, e);
+    am = fmaxf(fabsf(y0), fabsf(y1));
+  }
+}
+
+__device__ inline v8i gload32(const uint8_t* p) {
+  const uint4 a = reinterpret_cast<const uint4*>(p)[0];
+  const uint4 b = reinterpret_cast<const uint4*>(p)[1];
+  v8i r;
+  r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z; r[3] = (int)a.w;
+  r[4] = (int)b.x; r[5] = (int)b.y; r[6] = (int)b.z; r[7] = (int)b.w;
+  return r;
+}
+
+// Output of one query row held by a lane: O^T[d][query] for
+// d = 32 b + 8 (r / 4) + 4 gq + r % 4, scaled by inv, as bf16.
+template <int D>
+__device__ inline void store_rows(uint16_t* orow, const v16f (&O)[D / 32], float inv, int gq) {
 #pragma unroll
-  for (int c = 0; c < CPT / 8; ++c)
-    reinterpret_cast<uint4*>(dst)[c] = make_uint4(pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]);
+  for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const uint32_t lo = f32_to_bf16_rne(O[b][4 * g4] * inv) | (f32_to_bf16_rne(O[b][4 * g4 + 1] * inv) << 16);
+      const uint32_t hi = f32_to_bf16_rne(O[b][4 * g4 + 2] * inv) | (f32_to_bf16_rne(O[b][4 * g4 + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(orow + 32 * b + 8 * g4 + 4 * gq) = make_uint2(lo, hi);
+    }
 }
 
 // ---------------------------------------------------------------------------
 template <int D, int TERMS>
-__global__ __launch_bounds__(256, 1) void attend_kernel(AttnArgs A) {
+__global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
   constexpr int KS = D / 64, DB = D / 32;
-  constexpr int EPT = D / 8;  // query elements per thread in the Q prep
-  constexpr int CPT = D / 8;  // output columns per thread in the merges
   __shared__ AttnSmem<D> sm;
 
   const Geom& g = A.g;
   const int H = g.n_heads, N = g.n_slots, NP = g.n_pad, NT = g.n_tiles;
   const int G = (int)gridDim.x;
-  const int b = (int)blockIdx.x;
-  const int gi = G % 8 == 0 ? (b & 7) * (G / 8) + (b >> 3) : b;  // this workgroup's range
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int bid = (int)blockIdx.x;
+  const int gi = G % 8 == 0 ? (bid & 7) * (G / 8) + (bid >> 3) : bid;  // this workgroup's range
+  // 8 waves: wave w serves queries 32 (w % 4) .. + 31 of the unit and takes
+  // the tiles of parity w / 4 of each pair.  The wave index is uniform per
+  // wave; readfirstlane lets the compiler keep what derives from it in scalar
+  // registers.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int gw = wave >> 2, qw = wave & 3;
   const int li = lane & 31, gq = lane >> 5;
-  const int qrow = threadIdx.x >> 3, qpart = threadIdx.x & 7;  // Q prep: 8 threads per row
-  const int row = threadIdx.x & 31, part = threadIdx.x >> 5;   // merges: 8 column blocks
 
   const LayerPtrs L = layer_ptrs(g, A.layer);
   const int head = L.state[0], nv = L.state[1];
@@ -303,29 +477,30 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttnArgs A) {
     count = e < N ? e / kTile - T0 + 1 : (NT - T0) + (e - N) / kTile + 1;
     if (count > NT) count = NT;
   }
-  const int U = A.nqb * H;
+  const int U = A.nqg * H;
 
-  if (count == 0) {  // empty cache: every output row is zero
-    for (int u = gi; u < U; u += G) {
-      const int h = u / A.nqb, qi = 32 * (u % A.nqb) + row;
-      if (qi < A.n_q) {
-        uint4* dst = reinterpret_cast<uint4*>(A.out + ((size_t)qi * H + h) * D + part * CPT);
+  if (count == 0) {  // empty cache: every output row is zero (wave group 0 writes)
+    if (gw == 0) {
+      for (int u = gi; u < U; u += G) {
+        const int h = u / A.nqg, qi = kQG * (u % A.nqg) + 32 * qw + li;
+        if (qi < A.n_q) {
+          uint4* dst = reinterpret_cast<uint4*>(A.out + ((size_t)qi * H + h) * D + (D / 2) * gq);
 #pragma unroll
-        for (int c = 0; c < CPT / 8; ++c) dst[c] = make_uint4(0u, 0u, 0u, 0u);
+          for (int c = 0; c < D / 16; ++c) dst[c] = make_uint4(0u, 0u, 0u, 0u);
+        }
       }
     }
     return;
   }
 
+  const TileOffsets<D> off(lane);
+  const CopyOffsets<D> coff(qw, lane);
+  lds_u8* const kv0 = (lds_u8*)&sm.kv[0][0];  // the tile buffers, as LDS addresses
+  constexpr int KVB = TileLds<D>::BYTES;
+  constexpr int C = TileLds<D>::COPIES;
   const long long W = (long long)U * count;
   const long long r_lo = (long long)gi * W / G, r_hi = (long long)(gi + 1) * W / G;
   auto tile_of = [&](int kk) { const int T = T0 + kk; return T >= NT ? T - NT : T; };
-  auto tile_mask = [&](int T) {
-    const int sl = T * kTile + lane;
-    int rel = sl - a;
-    if (rel < 0) rel += N;
-    return __ballot(sl < N && rel < nv);
-  };
 
   for (long long x = r_lo; x < r_hi;) {
     const int u = (int)(x / count);
@@ -333,7 +508,8 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttnArgs A) {
     const long long rem = r_hi - x;
     const int t_hi = rem < count - t_lo ? t_lo + (int)rem : count;
     x += t_hi - t_lo;
-    const int h = u / A.nqb, qb = u % A.nqb;
+    const int nk = t_hi - t_lo;
+    const int h = u / A.nqg, qg = u % A.nqg;
     const float vmaxh = __uint_as_float(L.vmax[h]);
     const float ch = vmaxh > 0.f ? kE4M3Max / (4.f * vmaxh) : 1.f;
     TileSrc src;
@@ -342,201 +518,154 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttnArgs A) {
     src.skb = L.scale_k + (size_t)h * NP;
     src.svb = L.scale_v + (size_t)h * NP;
 
-    // ---- 1. queries: RoPE and one or two e4m3 terms, staged in LDS ----
-    {
-      const int iq = 32 * qb + qrow;
-      float y[EPT];
-      float am = 0.f;
-      if (iq < A.n_q) {
-        const uint4* qp = A.q + (((size_t)iq * H + h) * D + qpart * EPT) / 8;
-        const int32_t p = A.q_pos[iq];
-        const double* turns = omega_turns(g);
+    // Segment tile j lives in buffer j % kBufs; wave group j % 2 copies it
+    // and computes it.  Copies of the first kPairs - 1 pairs start before
+    // the query loads.
 #pragma unroll
-        for (int c = 0; c < EPT / 8; ++c) {
-          const uint4 w = qp[c];
-          const float xv[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                               bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            float cs, sn;
-            rope_cs(p, turns[qpart * EPT / 2 + 4 * c + m], cs, sn);
-            y[8 * c + 2 * m] = xv[2 * m] * cs - xv[2 * m + 1] * sn;
-            y[8 * c + 2 * m + 1] = xv[2 * m] * sn + xv[2 * m + 1] * cs;
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) am = fmaxf(am, fabsf(y[e]));
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) y[e] = 0.f;
-      }
-#pragma unroll
-      for (int t = 0; t < TERMS; ++t) {
-        am = group_max<8>(am);
-        const int e = am > 0.f ? pow2_exponent(am) : 0;
-        uint32_t wd[EPT / 4];
-#pragma unroll
-        for (int c = 0; c < EPT / 4; ++c) {
-          const uint32_t w = pack2_fp8<false>(clamp448(ldexpf(y[4 * c], -e)), clamp448(ldexpf(y[4 * c + 1], -e)), 0u);
-          wd[c] = pack2_fp8<true>(clamp448(ldexpf(y[4 * c + 2], -e)), clamp448(ldexpf(y[4 * c + 3], -e)), w);
-        }
-        uint8_t* dst = sm.q[t] + qrow * (D + 16) + qpart * EPT;
-        if constexpr (EPT == 16) {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-        } else {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(wd[0], wd[1]);
-        }
-        if (qpart == 0) sm.qexp[t][qrow] = e;
-        // residual for the next term
-        am = 0.f;
-#pragma unroll
-        for (int c = 0; c < EPT / 4; ++c) {
-          float d0, d1, d2, d3;
-          unpack4_fp8(wd[c], d0, d1, d2, d3);
-          y[4 * c] -= ldexpf(d0, e);
-          y[4 * c + 1] -= ldexpf(d1, e);
-          y[4 * c + 2] -= ldexpf(d2, e);
-          y[4 * c + 3] -= ldexpf(d3, e);
-        }
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) am = fmaxf(am, fabsf(y[k]));
-      }
+    for (int j = 0; j < kPairs - 1; ++j) {
+      const int tj = 2 * j + gw;
+      if (tj < nk) copy_tile<D>(kv0 + (tj % kBufs) * KVB, src, tile_of(t_lo + tj), coff, qw, lane);
     }
-    __syncthreads();
+
+    // ---- 1. this wave's 32 prepared queries (B operand of S^T = K Q^T) ----
+    const int qi = kQG * qg + 32 * qw + li;
     v8i qf[TERMS][KS];
     int qs[TERMS];
 #pragma unroll
     for (int t = 0; t < TERMS; ++t) {
-      const uint8_t* qp = sm.q[t] + li * (D + 16) + 32 * gq;
+      const size_t row = ((size_t)t * H + h) * A.ws.nq_pad + qi;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[t][ks] = load32(qp + 64 * ks, qp + 64 * ks + 16);
-      qs[t] = 127 + sm.qexp[t][li];
+      for (int ks = 0; ks < KS; ++ks) qf[t][ks] = gload32(A.ws.qcodes + row * D + 64 * ks + 32 * gq);
+      qs[t] = 127 + A.ws.qexp[row];
     }
 
-    // ---- 2. this wave's tiles t_lo + wave, +4, ...: software pipelined ----
+    // ---- 2. the segment's tiles, two at a time (one per wave group) ----
     WaveState<D> st;
     st.m = -INFINITY;
     st.l = 0.f;
 #pragma unroll
     for (int bb = 0; bb < DB; ++bb) st.O[bb] = v16f{};
-    const int first = t_lo + wave;
-    const int nw = first < t_hi ? (t_hi - first + 3) / 4 : 0;
-    if (nw > 0) {
-      KOp<D> kf;
-      VOp<D> v0, v1;
-      v16f s0[2], s1[2];
-      load_k<D>(kf, src, tile_of(first), lane);
-      load_v<D>(v0, src, tile_of(first), lane);
-      qk<D, TERMS>(s0, kf, qf, qs);
-      if (nw > 1) load_k<D>(kf, src, tile_of(first + 4), lane);
-      for (int j = 0; j < nw; j += 2) {
-        // tile j: S in s0, V in v0; K of tile j + 1 in kf
-        if (j + 1 < nw) {
-          qk<D, TERMS>(s1, kf, qf, qs);
-          if (j + 2 < nw) load_k<D>(kf, src, tile_of(first + 4 * (j + 2)), lane);
-          load_v<D>(v1, src, tile_of(first + 4 * (j + 1)), lane);
-        }
-        softmax_pv<D, TERMS>(s0, v0, st, tile_mask(tile_of(first + 4 * j)), A.kscale, ch, lane);
-        if (j + 1 >= nw) break;
-        // tile j + 1: S in s1, V in v1; K of tile j + 2 in kf
-        if (j + 2 < nw) {
-          qk<D, TERMS>(s0, kf, qf, qs);
-          if (j + 3 < nw) load_k<D>(kf, src, tile_of(first + 4 * (j + 3)), lane);
-          load_v<D>(v0, src, tile_of(first + 4 * (j + 2)), lane);
-        }
-        softmax_pv<D, TERMS>(s1, v1, st, tile_mask(tile_of(first + 4 * (j + 1))), A.kscale, ch, lane);
+    const int npairs = (nk + 1) >> 1;
+    const int last = (nk - 1 - gw) >> 1;  // last pair holding a tile of this group (-1: none)
+    for (int i = 0; i < npairs; ++i) {
+      const int tj = 2 * i + gw;
+      // this wave's copies of the group's next pair may stay in flight
+      if (last - i >= 1) wait_copies_and_barrier<C>();
+      else wait_copies_and_barrier<0>();
+      if (tj < nk) {
+        const lds_u8* lb = kv0 + (tj % kBufs) * KVB;
+        KOp<D> kf;
+        VOp<D> vf;
+        v16f sacc[2];
+        read_k<D>(kf, lb, off);
+        qk<D, TERMS>(sacc, kf, qf, qs);
+        read_v<D>(vf, lb, off);
+        // the buffer of this group's previous tile was last read before the
+        // barrier above: refill it with the group's tile kPairs - 1 pairs on
+        const int tn = tj + 2 * (kPairs - 1);
+        if (tn < nk) copy_tile<D>(kv0 + (tn % kBufs) * KVB, src, tile_of(t_lo + tn), coff, qw, lane);
+        const int T = tile_of(t_lo + tj);
+        const int sl = T * kTile + lane;
+        int rel = sl - a;
+        if (rel < 0) rel += N;
+        const unsigned long long mask = __ballot(sl < N && rel < nv);
+        softmax_pv<D, TERMS>(sacc, vf, st, mask, A.kscale, ch, lane);
       }
     }
 
-    // ---- 3. merge the 4 waves in LDS ----
+    // ---- 3. merge the two wave groups through LDS (the tile buffers are free:
+    //         every copy has been waited for) ----
+    __syncthreads();
     {
-      const float l = half_swap_add(st.l);
-      float* sO = sm.merge[wave];
+      constexpr int MS = (DB * 16 + 2) * 64;  // floats per query block
+      typedef __attribute__((address_space(3))) float lds_f;
+      lds_f* mb = reinterpret_cast<lds_f*>(kv0) + qw * MS;
+      if (gw == 1) {
 #pragma unroll
-      for (int bb = 0; bb < DB; ++bb)
+        for (int bb = 0; bb < DB; ++bb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sO[(32 * bb + 8 * (r >> 2) + 4 * gq + (r & 3)) * 32 + li] = st.O[bb][r];
-      if (gq == 0) {
-        sO[32 * D + li] = st.m;
-        sO[32 * D + 32 + li] = l;
+          for (int r = 0; r < 16; ++r) mb[(bb * 16 + r) * 64 + lane] = st.O[bb][r];
+        mb[DB * 16 * 64 + lane] = st.m;
+        mb[DB * 16 * 64 + 64 + lane] = st.l;
+      }
+      __syncthreads();
+      if (gw == 0) {
+        const float m1 = mb[DB * 16 * 64 + lane], l1 = mb[DB * 16 * 64 + 64 + lane];
+        const float M = fmaxf(st.m, m1);  // st.m is finite: group 0 always has a tile
+        const float a0 = __builtin_amdgcn_exp2f(st.m - M), a1 = __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st.O[bb][r] = a0 * st.O[bb][r] + a1 * mb[(bb * 16 + r) * 64 + lane];
+        st.l = a0 * st.l + a1 * l1;
+        st.m = M;
       }
     }
-    __syncthreads();
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.merge[w][32 * D + row]);
-    float wt[4], Ls = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      wt[w] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm.merge[w][32 * D + row] - M);
-      Ls += wt[w] * sm.merge[w][32 * D + 32 + row];
-    }
-    float o[CPT];
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int d = part * CPT + c;
-      o[c] = wt[0] * sm.merge[0][d * 32 + row] + wt[1] * sm.merge[1][d * 32 + row] +
-             wt[2] * sm.merge[2][d * 32 + row] + wt[3] * sm.merge[3][d * 32 + row];
-    }
-    const int qi = 32 * qb + row;
-    uint16_t* orow = A.out + ((size_t)qi * H + h) * D + part * CPT;
 
     // ---- 4. whole unit: output; split unit: partial, the last to finish merges ----
+    const float Lw = half_swap_add(st.l);
+    uint16_t* orow = A.out + ((size_t)qi * H + h) * D;
     if (t_lo == 0 && t_hi == count) {
-      if (qi < A.n_q) store_out<CPT>(orow, o, Ls > 0.f ? 1.f / (ch * Ls) : 0.f);
+      if (gw == 0 && qi < A.n_q) store_rows<D>(orow, st.O, Lw > 0.f ? 1.f / (ch * Lw) : 0.f, gq);
     } else {
       // Partial id gi + u is distinct for every (workgroup, unit) pair: ranges
       // are ordered, so a later workgroup never meets an earlier unit.
       const size_t seg = (size_t)gi + u;
-      float4* po = reinterpret_cast<float4*>(A.ws.part_o + (seg * 32 + row) * D + part * CPT);
+      // Partials travel through device-coherent accesses (relaxed atomics at
+      // agent scope: stores and loads that bypass the per-XCD caches), so no
+      // fence has to write back or invalidate a whole L2.  Each thread's
+      // stores complete (vmcnt 0) before the barrier, and the barrier before
+      // the counter update; the finisher reads only after the counter says
+      // every segment has stored.
+      if (gw == 0) {
+        float* po = A.ws.part_o + (seg * 4 + qw) * (size_t)(DB * 16 * 64);
 #pragma unroll
-      for (int c = 0; c < CPT / 4; ++c) po[c] = make_float4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
-      if (part == 0) {
-        A.ws.part_ml[(seg * 32 + row) * 2] = M;
-        A.ws.part_ml[(seg * 32 + row) * 2 + 1] = Ls;
+        for (int bb = 0; bb < DB; ++bb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            __hip_atomic_store(po + (bb * 16 + r) * 64 + lane, st.O[bb][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float* pml = A.ws.part_ml + ((seg * 4 + qw) * 64 + lane) * 2;
+        __hip_atomic_store(pml, st.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(pml + 1, Lw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-      // release this partial device-wide, then add this segment's tiles to
-      // the unit's counter; whoever completes the count merges
-      __threadfence();
       __syncthreads();
       if (threadIdx.x == 0) {
-        const int prev = atomicAdd(&A.ws.count[u], t_hi - t_lo);
-        sm.flag = prev + (t_hi - t_lo) == count;
+        const int prev = __hip_atomic_fetch_add(&A.ws.count[u], nk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm.flag = prev + nk == count;
       }
       __syncthreads();
-      if (sm.flag) {
-        __threadfence();  // acquire the other segments' partials
+      if (sm.flag && gw == 0) {
         const long long ulo = (long long)u * count, uhi = ulo + count;
         // segments of unit u, in order: the workgroup range holding tile-unit
         // y is floor(((y + 1) G - 1) / W); the next segment starts at its end
         float Mu = -INFINITY;
         for (long long y = ulo; y < uhi;) {
           const long long w = ((y + 1) * G - 1) / W;
-          Mu = fmaxf(Mu, A.ws.part_ml[(((size_t)w + u) * 32 + row) * 2]);
+          const float* ml = A.ws.part_ml + ((((size_t)w + u) * 4 + qw) * 64 + lane) * 2;
+          Mu = fmaxf(Mu, __hip_atomic_load(ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
           y = (w + 1) * W / G;
         }
-        float acc[CPT];
+        v16f acc[DB];
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
+        for (int bb = 0; bb < DB; ++bb) acc[bb] = v16f{};
         float Lu = 0.f;
         for (long long y = ulo; y < uhi;) {
           const long long w = ((y + 1) * G - 1) / W;
-          const size_t id = ((size_t)w + u) * 32 + row;
-          const float sc = __builtin_amdgcn_exp2f(A.ws.part_ml[id * 2] - Mu);
-          Lu += sc * A.ws.part_ml[id * 2 + 1];
-          const float4* p4 = reinterpret_cast<const float4*>(A.ws.part_o + id * D + part * CPT);
+          const size_t sid = ((size_t)w + u) * 4 + qw;
+          const float* ml = A.ws.part_ml + (sid * 64 + lane) * 2;
+          const float sc = __builtin_amdgcn_exp2f(__hip_atomic_load(ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - Mu);
+          Lu += sc * __hip_atomic_load(ml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const float* ps = A.ws.part_o + sid * (size_t)(DB * 16 * 64);
 #pragma unroll
-          for (int c = 0; c < CPT / 4; ++c) {
-            const float4 v4 = p4[c];
-            acc[4 * c] += sc * v4.x;
-            acc[4 * c + 1] += sc * v4.y;
-            acc[4 * c + 2] += sc * v4.z;
-            acc[4 * c + 3] += sc * v4.w;
-          }
+          for (int bb = 0; bb < DB; ++bb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              acc[bb][r] += sc * __hip_atomic_load(ps + (bb * 16 + r) * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           y = (w + 1) * W / G;
         }
-        if (qi < A.n_q) store_out<CPT>(orow, acc, Lu > 0.f ? 1.f / (ch * Lu) : 0.f);
-        if (threadIdx.x == 0) A.ws.count[u] = 0;  // ready for the next call
+        if (qi < A.n_q) store_rows<D>(orow, acc, Lu > 0.f ? 1.f / (ch * Lu) : 0.f, gq);
+        if (threadIdx.x == 0) __hip_atomic_store(&A.ws.count[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();  // LDS is reused by the next segment
@@ -546,23 +675,43 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttnArgs A) {
 hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void* q,
                          const int32_t* q_pos, int n_q, void* out, hipStream_t s) {
   const int D = g.head_dim;
+  const int nqg = (n_q + kQG - 1) / kQG;
+  QPrepArgs P;
+  P.g = g;
+  P.ws = ws;
+  P.n_q = n_q;
+  P.nq_rows = nqg * kQG;
+  P.q = (const uint32_t*)q;
+  P.q_pos = q_pos;
+  const int rows = g.n_heads * P.nq_rows, rows_per_block = 4 * (128 / D);
+  const dim3 pgrid((rows + rows_per_block - 1) / rows_per_block);
+  if (D == 128) {
+    if (ws.terms == 2) hipLaunchKernelGGL((q_prep_kernel<128, 2>), pgrid, dim3(256), 0, s, P);
+    else hipLaunchKernelGGL((q_prep_kernel<128, 1>), pgrid, dim3(256), 0, s, P);
+  } else {
+    if (ws.terms == 2) hipLaunchKernelGGL((q_prep_kernel<64, 2>), pgrid, dim3(256), 0, s, P);
+    else hipLaunchKernelGGL((q_prep_kernel<64, 1>), pgrid, dim3(256), 0, s, P);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
   AttnArgs A;
   A.g = g;
   A.ws = ws;
   A.layer = layer;
   A.n_q = n_q;
-  A.nqb = (n_q + 31) / 32;
+  A.nqg = nqg;
   A.q = (const uint4*)q;
   A.q_pos = q_pos;
   A.out = (uint16_t*)out;
   A.kscale = kLog2e / sqrtf((float)D);
   const dim3 grid(ws.grid);
   if (D == 128) {
-    if (ws.terms == 2) hipLaunchKernelGGL((attend_kernel<128, 2>), grid, dim3(256), 0, s, A);
-    else hipLaunchKernelGGL((attend_kernel<128, 1>), grid, dim3(256), 0, s, A);
+    if (ws.terms == 2) hipLaunchKernelGGL((attend_kernel<128, 2>), grid, dim3(512), 0, s, A);
+    else hipLaunchKernelGGL((attend_kernel<128, 1>), grid, dim3(512), 0, s, A);
   } else {
-    if (ws.terms == 2) hipLaunchKernelGGL((attend_kernel<64, 2>), grid, dim3(256), 0, s, A);
-    else hipLaunchKernelGGL((attend_kernel<64, 1>), grid, dim3(256), 0, s, A);
+    if (ws.terms == 2) hipLaunchKernelGGL((attend_kernel<64, 2>), grid, dim3(512), 0, s, A);
+    else hipLaunchKernelGGL((attend_kernel<64, 1>), grid, dim3(512), 0, s, A);
   }
   return hipGetLastError();
 }

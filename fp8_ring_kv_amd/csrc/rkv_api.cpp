@@ -43,7 +43,7 @@ int compute_units() {
 struct Plan {
   rkv::Geom g;
   rkv::AttnWs ws;  // pointers filled relative to base 0 (offsets) until create
-  size_t ws_parto, ws_partml, ws_count;
+  size_t ws_parto, ws_partml, ws_count, ws_qcodes, ws_qexp;
   size_t total;
 };
 
@@ -98,21 +98,28 @@ Plan make_plan(const rkv_params* p) {
   g.layer_bytes = o;
 
   size_t w = g.layer0 + (size_t)p->n_layers * g.layer_bytes;
-  // Attention workspace: one partial result (32 query rows) per segment of
-  // the persistent grid -- at most units + workgroups of them -- and one
-  // arrival counter per unit.
-  const size_t nqb = align_up((size_t)p->max_queries, 32) / 32;
-  const size_t units = nqb * H;
+  // Attention workspace: one partial result per segment of the persistent
+  // grid -- at most units + workgroups of them, each 128 query rows x D fp32
+  // plus (max, sum) per row and half-wave -- and one arrival counter per unit
+  // (unit = head x 128-query group).
+  const size_t nqg = align_up((size_t)p->max_queries, 128) / 128;
+  const size_t units = nqg * H;
   const int grid = p->attn_workgroups > 0 ? p->attn_workgroups : compute_units();
   const size_t segs = units + (size_t)grid;
   pl.ws.grid = grid;
   pl.ws.terms = p->precision == RKV_PRECISE ? 2 : 1;
   pl.ws_parto = w;
-  w = align_up(w + segs * 32 * D * 4, kAlign);
+  w = align_up(w + segs * 128 * D * 4, kAlign);
   pl.ws_partml = w;
-  w = align_up(w + segs * 32 * 2 * 4, kAlign);
+  w = align_up(w + segs * 4 * 64 * 2 * 4, kAlign);
   pl.ws_count = w;
   w = align_up(w + units * 4, kAlign);
+  // prepared queries: two e4m3 terms per element and an exponent per row and term
+  pl.ws.nq_pad = (int32_t)(nqg * 128);
+  pl.ws_qcodes = w;
+  w = align_up(w + 2 * (size_t)H * pl.ws.nq_pad * D, kAlign);
+  pl.ws_qexp = w;
+  w = align_up(w + 2 * (size_t)H * pl.ws.nq_pad * 4, kAlign);
   pl.total = w;
   return pl;
 }
@@ -163,6 +170,8 @@ int ring_cache_create(const rkv_params* p, void* dev_buf, size_t bytes, hipStrea
   c->ws.part_o = reinterpret_cast<float*>(c->g.base + pl.ws_parto);
   c->ws.part_ml = reinterpret_cast<float*>(c->g.base + pl.ws_partml);
   c->ws.count = reinterpret_cast<int32_t*>(c->g.base + pl.ws_count);
+  c->ws.qcodes = c->g.base + pl.ws_qcodes;
+  c->ws.qexp = reinterpret_cast<int32_t*>(c->g.base + pl.ws_qexp);
   c->bytes = pl.total;
   const int half = p->head_dim / 2;
   for (int j = 0; j < half; ++j) {

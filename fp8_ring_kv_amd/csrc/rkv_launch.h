@@ -11,9 +11,12 @@ namespace rkv {
 
 // Attention workspace inside the cache buffer (shared by all layers).
 struct AttnWs {
-  float* part_o;   // [units + grid][32][D] fp32 partial outputs of split units
-  float* part_ml;  // [units + grid][32][2] fp32 partial (running max, sum)
+  float* part_o;   // [units + grid][4 waves][D/32][16][64 lanes] fp32 partial outputs
+  float* part_ml;  // [units + grid][4 waves][64 lanes] fp32 pairs (running max, sum)
   int32_t* count;  // [units] arrival counters of split units (zero between calls)
+  uint8_t* qcodes; // [2 terms][H][nq_pad][D] e4m3 codes of the RoPE'd queries
+  int32_t* qexp;   // [2 terms][H][nq_pad] power-of-two exponent of each query row and term
+  int32_t nq_pad;  // max_queries rounded up to 128
   int32_t grid;    // persistent workgroups
   int32_t terms;   // 2 = precise, 1 = fast
 };
