@@ -245,14 +245,15 @@ class RingCache:
         return self.buf[off:off + nbytes].view(dtype)
 
     def state(self, layer: int) -> torch.Tensor:
-        """(head, n_valid, ticket, 0) int32 on device."""
+        """(head, n_valid, ...) int32 on device (entries past the first two are
+        counters internal to the write kernel)."""
         lay = self.layout(layer)
-        return self._view(lay.state, 16, torch.int32)
+        return self._view(lay.state, 48, torch.int32)
 
     def vmax(self, layer: int) -> torch.Tensor:
         """[H] float32: largest value scale written to each head since the reset."""
         lay = self.layout(layer)
-        return self._view(lay.vmax, 4 * self.n_heads, torch.float32)
+        return self._view(lay.vmax, 4 * 8 * self.n_heads, torch.float32).view(self.n_heads, 8).amax(dim=1)
 
     def slot_pos(self, layer: int) -> torch.Tensor:
         lay = self.layout(layer)

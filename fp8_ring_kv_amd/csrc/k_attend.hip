@@ -398,15 +398,16 @@ __global__ __launch_bounds__(256) void q_prep_kernel(QPrepArgs A) {
   if (r >= H * A.nq_rows) return;  // whole rows only: the reductions stay inside live lanes
   const int j = lane % LPR;
   const int h = r / A.nq_rows, qi = r % A.nq_rows;
-  float y0 = 0.f, y1 = 0.f;
-  if (qi < A.n_q) {
-    const uint32_t w = A.q[((size_t)qi * H + h) * (D / 2) + j];
-    float cs, sn;
-    rope_cs(A.q_pos[qi], omega_turns(A.g)[j], cs, sn);
-    const float x0 = bf16_lo(w), x1 = bf16_hi(w);
-    y0 = x0 * cs - x1 * sn;
-    y1 = x0 * sn + x1 * cs;
-  }
+  // rows past n_q read row n_q - 1 (every load in range, no branch around
+  // the loads) and are zeroed
+  const bool active = qi < A.n_q;
+  const int qr = active ? qi : A.n_q - 1;
+  const uint32_t w = A.q[((size_t)qr * H + h) * (D / 2) + j];
+  float cs, sn;
+  rope_cs(A.q_pos[qr], omega_turns(A.g)[j], cs, sn);
+  const float x0 = active ? bf16_lo(w) : 0.f, x1 = active ? bf16_hi(w) : 0.f;
+  float y0 = x0 * cs - x1 * sn;
+  float y1 = x0 * sn + x1 * cs;
   float am = fmaxf(fabsf(y0), fabsf(y1));
 #pragma unroll
   for (int t = 0; t < TERMS; ++t) {
@@ -510,7 +511,10 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
     x += t_hi - t_lo;
     const int nk = t_hi - t_lo;
     const int h = u / A.nqg, qg = u % A.nqg;
-    const float vmaxh = __uint_as_float(L.vmax[h]);
+    uint32_t vm = 0u;  // the head's bound: max over its kSub slots (bit order = value order)
+#pragma unroll
+    for (int k2 = 0; k2 < kSub; ++k2) vm = max(vm, L.vmax[h * kSub + k2]);
+    const float vmaxh = __uint_as_float(vm);
     const float ch = vmaxh > 0.f ? kE4M3Max / (4.f * vmaxh) : 1.f;
     TileSrc src;
     src.kbase = L.codes_k + (size_t)h * NP * D;

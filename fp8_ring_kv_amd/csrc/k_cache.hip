@@ -55,8 +55,9 @@ __global__ void reset_kernel(Geom g, int layer_lo) {
   const LayerPtrs L = layer_ptrs(g, layer_lo + (int)blockIdx.y);
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < g.n_pad) L.slot_pos[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x < 4) L.state[threadIdx.x] = 0;
-  if (blockIdx.x == 0 && (int)threadIdx.x < g.n_heads) L.vmax[threadIdx.x] = 0u;
+  if (blockIdx.x == 0 && threadIdx.x < kStateInts) L.state[threadIdx.x] = 0;
+  if (blockIdx.x == 0)
+    for (int j = (int)threadIdx.x; j < g.n_heads * kSub; j += (int)blockDim.x) L.vmax[j] = 0u;
 }
 
 hipError_t launch_reset(const Geom& g, int layer_lo, int layer_hi, hipStream_t s) {
@@ -111,14 +112,28 @@ __global__ __launch_bounds__(16 * (D / 8)) void write_rope_fp8_kernel(
     }
     p = pos[i];
   }
+  // Tickets for the device-side write position, taken once head and n_valid
+  // are read (and after the row loads are issued: a returning atomic holds
+  // up every later load's wait): whoever takes the last ticket knows every
+  // workgroup has read them and may advance them.  Workgroup w takes a ticket on
+  // sub-counter w % kSub; the last arrival of each sub-group takes one on the
+  // top counter, so no counter sees more than ceil(total / kSub) atomics.
+  // The increment depends on the loaded head (it is always 1), so it cannot
+  // be issued before the load returns.  No workgroup reads what another one
+  // writes, so relaxed device-scope atomics suffice; the next kernel on the
+  // stream sees the new state.
+  // (The returned ticket is looked at only at the end of the kernel.)
+  const int wg = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+  int t1 = 0;
+  if (threadIdx.x == 0)
+    t1 = __hip_atomic_fetch_add(&L.state[4 + wg % kSub], head < 0x7FFFFFFF ? 1 : 2, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+  // angles for every lane (the table index is always in range; inactive
+  // lanes rotate zeros), so the four table loads issue together
   float cs[4], sn[4];
   const double* turns = omega_turns(g);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    cs[m] = 1.f;
-    sn[m] = 0.f;
-    if (active) rope_cs(p, turns[4 * lane + m], cs[m], sn[m]);
-  }
+  for (int m = 0; m < 4; ++m) rope_cs(p, turns[4 * lane + m], cs[m], sn[m]);
 
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh) {
@@ -164,15 +179,9 @@ __global__ __launch_bounds__(16 * (D / 8)) void write_rope_fp8_kernel(
     if (lane == 0) vmx[hh][tau] = active ? sv : 0.f;
   }
   if (active && lane == 0 && h0 == 0) L.slot_pos[slot] = p;
-  __syncthreads();
-  // running per-head maximum of the value scales (non-negative floats order
-  // like their bit patterns)
-  if ((int)threadIdx.x < HG) {
-    float mx = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, vmx[threadIdx.x][e]);
-    if (mx > 0.f) atomicMax(&L.vmax[h0 + threadIdx.x], __float_as_uint(mx));
-  }
+  // LDS-only barrier: the transpose below needs the LDS writes above, not
+  // the global stores (a __syncthreads fence would wait for those too)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // V: transposed 64-slot tiles, row d holds the tile's slots in order.  The
   // group's 16 slots are 16 consecutive bytes of each row; thread t writes
@@ -211,19 +220,29 @@ __global__ __launch_bounds__(16 * (D / 8)) void write_rope_fp8_kernel(
     }
   }
 
-  // The last workgroup to finish advances the device-side write position.
-  // Every workgroup has consumed head/n_valid before it takes its ticket and
-  // no workgroup reads what another one wrote, so the ticket needs no fence:
-  // a relaxed device-scope atomic orders the counter itself, and the next
-  // kernel on the stream sees the new state.
-  __syncthreads();
+  // Running per-head maximum of the value scales (non-negative floats order
+  // like their bit patterns); nothing waits for these atomics.
+  if ((int)threadIdx.x < HG) {
+    float mx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, vmx[threadIdx.x][e]);
+    if (mx > 0.f) atomicMax(&L.vmax[(h0 + threadIdx.x) * kSub + blockIdx.x % kSub], __float_as_uint(mx));
+  }
+  // The last arrival of each sub-group takes a ticket on the top counter;
+  // the last of those advances the write position.
   if (threadIdx.x == 0) {
-    const int total = gridDim.x * gridDim.y;
-    const int prev = __hip_atomic_fetch_add(&L.state[2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev == total - 1) {
-      L.state[0] = (int)(((long long)head + n) % N);
-      L.state[1] = nvalid + n < N ? nvalid + n : N;
-      L.state[2] = 0;
+    const int total = (int)(gridDim.x * gridDim.y);
+    const int k = wg % kSub;
+    const int ksize = (total - k + kSub - 1) / kSub;  // workgroups with wg % kSub == k
+    const int nsub = total < kSub ? total : kSub;
+    if (t1 == ksize - 1) {
+      __hip_atomic_store(&L.state[4 + k], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int t2 = __hip_atomic_fetch_add(&L.state[2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t2 == nsub - 1) {
+        __hip_atomic_store(&L.state[2], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        L.state[0] = (int)(((long long)head + n) % N);
+        L.state[1] = nvalid + n < N ? nvalid + n : N;
+      }
     }
   }
 }

@@ -92,9 +92,9 @@ Plan make_plan(const rkv_params* p) {
   g.off_slot_pos = o;
   o = align_up(o + NP * 4, kAlign);
   g.off_state = o;
-  o = align_up(o + 16, kAlign);
+  o = align_up(o + rkv::kStateInts * 4, kAlign);
   g.off_vmax = o;
-  o = align_up(o + H * 4, kAlign);
+  o = align_up(o + H * rkv::kSub * 4, kAlign);
   g.layer_bytes = o;
 
   size_t w = g.layer0 + (size_t)p->n_layers * g.layer_bytes;

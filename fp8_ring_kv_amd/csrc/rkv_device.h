@@ -12,6 +12,10 @@ namespace rkv {
 constexpr float kE4M3Max = 448.0f;
 constexpr int kTile = 64;        // slots per attention tile and per V transpose tile
 constexpr int kMaxHalfDim = 64;  // D/2 for the largest supported head_dim (128)
+// Per-layer counters and maxima are spread over kSub slots so that no single
+// address takes more than a fraction of one launch's atomics.
+constexpr int kSub = 8;
+constexpr int kStateInts = 4 + kSub;  // head, n_valid, top counter, 0, sub-counters
 
 // Byte offsets of one layer's arrays (relative to the layer's start) and the
 // sizes every kernel needs.  Passed by value as a kernel argument.
@@ -31,8 +35,9 @@ struct LayerPtrs {
   float* scale_k;
   float* scale_v;
   int32_t* slot_pos;
-  int32_t* state;  // {head, n_valid, ticket, 0}
-  uint32_t* vmax;  // [H] largest value scale written since the reset (fp32 bits)
+  int32_t* state;  // {head, n_valid, top counter, 0, sub-counters[kSub]}
+  uint32_t* vmax;  // [H][kSub] largest value scale written since the reset (fp32
+                   // bits); the head's bound is the max over its kSub entries
 };
 
 __host__ __device__ inline LayerPtrs layer_ptrs(const Geom& g, int layer) {
@@ -82,10 +87,14 @@ __device__ inline float quant_div(float y, float s, float r) {
   const uint32_t a = b & 0x7FFFFFFFu;
   // midpoint test: normal e4m3 range (|q| >= 2^-6): the 20 fp32 mantissa bits
   // below the 3 e4m3 ones are 1000...0; subnormal range: 1024 |q| is odd.
+  // Evaluated without short-circuits so that it compiles to selects.
   const float t = __uint_as_float(a) * 1024.f;
-  const bool mid = a >= 0x3C800000u ? (a & 0xFFFFFu) == 0x80000u
-                                    : (t == rintf(t) && (((int)t) & 1));
-  if (mid && res != 0.f) q = __uint_as_float(b + (((res > 0.f) == (q > 0.f)) ? 1u : 0xFFFFFFFFu));
+  const bool normal = a >= 0x3C800000u;
+  const bool mid_n = (a & 0xFFFFFu) == 0x80000u;
+  const bool mid_s = (t == rintf(t)) & ((((int)t) & 1) != 0);
+  const bool adj = (normal ? mid_n : mid_s) & (res != 0.f);
+  const uint32_t step = ((res > 0.f) == (q > 0.f)) ? 1u : 0xFFFFFFFFu;
+  q = __uint_as_float(b + (adj ? step : 0u));
   return clamp448(q);
 }
 
@@ -127,11 +136,30 @@ __device__ inline float quant_mul(float y, float r) {
   return __builtin_amdgcn_fmed3f(y * r, -kE4M3Max, kE4M3Max);
 }
 
-// Max over the `width` lanes of an aligned lane group (width a power of two <= 64).
+// DPP move of a float (every lane reads a lane of its own 16-lane row).
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Max over each aligned group of W lanes (W = 2 .. 64), with DPP steps inside
+// 16-lane rows (rotate by 8, mirror within 8, swap within 4 and 2) and lane
+// swaps across rows (permlane16/32 swap): no LDS round trips.
 template <int W>
 __device__ inline float group_max(float v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, W));
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "group width");
+  if constexpr (W >= 16) v = fmaxf(v, dpp_f<0x128>(v));  // row_ror:8
+  if constexpr (W >= 8) v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+  if constexpr (W >= 4) v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0xB1>(v));                          // quad_perm [1,0,3,2]
+  if constexpr (W >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    v = fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+  }
+  if constexpr (W >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    v = fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+  }
   return v;
 }
 

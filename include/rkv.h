@@ -82,13 +82,15 @@ typedef struct {
  *   scale_k  f32 [H][N_pad]           per-(slot, head) key scale
  *   scale_v  f32 [H][N_pad]           per-(slot, head) value scale
  *   slot_pos i32 [N_pad]              position each slot was written with
- *   state    i32 [4]                  {head, n_valid, ticket, 0}: the next
- *                                      write slot, the number of valid slots
- *                                      (the cyclic range [head-n_valid, head)),
- *                                      and a kernel-internal counter.
- *   vmax     f32 [H]                  per head, the largest value scale
+ *   state    i32 [12]                 {head, n_valid, ...}: the next write
+ *                                      slot and the number of valid slots
+ *                                      (the cyclic range [head-n_valid,
+ *                                      head)); the other ten are counters
+ *                                      internal to the write kernel.
+ *   vmax     f32 [H][8]               per head, the largest value scale
  *                                      written since the last reset (an upper
- *                                      bound of every cached value scale). */
+ *                                      bound of every cached value scale) is
+ *                                      the max of the head's 8 entries. */
 typedef struct {
   size_t codes_k, codes_v, scale_k, scale_v, slot_pos, state, vmax;
   size_t layer_bytes; /* distance between consecutive layers */

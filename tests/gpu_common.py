@@ -76,6 +76,12 @@ def assert_cache_matches(cache, layer, st, slots=None, check_v=True, pre=None):
     from oracle import ring as oring
     (head, nv), sp, ck, cv, sk, sv = readback(cache, layer)
     assert (head, nv) == (st.head, st.n_valid), ((head, nv), (st.head, st.n_valid))
+    # the write kernel's internal counters are back at zero after every call
+    counters = cache.state(layer).cpu().numpy()[2:12]
+    assert not counters.any(), counters
+    # the per-head value-scale bound equals the oracle's (fp32 values)
+    vmax = cache.vmax(layer).cpu().numpy().astype(np.float64)
+    assert np.array_equal(vmax, st.vmax), (vmax, st.vmax)
     valid = oring.valid_slots(st) if slots is None else slots
     assert np.array_equal(sp[valid], st.slot_pos[valid])
     extra = None
