@@ -346,13 +346,16 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
       st.l += p;
       x[e] = p * bcast16(sub ? svx1 : svx0, r0 + e);
     }
-    uint32_t hw = pack2_fp8<false>(x[0], x[1], 0u);
+    // (the low-half conversion keeps the high half of its third operand,
+    // which the high-half conversion overwrites: any register will do)
+    uint32_t hw = pack2_fp8<false>(x[0], x[1], __float_as_uint(x[0]));
     hw = pack2_fp8<true>(x[2], x[3], hw);
     ph[w] = (int)hw;
     if (TERMS == 2) {  // second term: 16 (x - e4m3(x)), descaled by 2^-4
       float d0, d1, d2, d3;
       unpack4_fp8(hw, d0, d1, d2, d3);
-      uint32_t lw = pack2_fp8<false>((x[0] - d0) * 16.f, (x[1] - d1) * 16.f, 0u);
+      const float l0 = (x[0] - d0) * 16.f;
+      uint32_t lw = pack2_fp8<false>(l0, (x[1] - d1) * 16.f, __float_as_uint(l0));
       lw = pack2_fp8<true>((x[2] - d2) * 16.f, (x[3] - d3) * 16.f, lw);
       pl[w] = (int)lw;
     }
@@ -378,50 +381,81 @@ struct __attribute__((aligned(16))) AttnSmem {
 // e_t the smallest exponent that fits the row (448 * 2^e_t >= amax), y_0 = y
 // and y_{t+1} the residual; the E8M0 operand 127 + e_t of the matrix
 // instruction applies 2^e_t exactly.  Rows n_q .. nq_rows - 1 are zero.
-// One lane per RoPE pair; D/2 lanes per row.
+// 8 threads per row, each with D/16 RoPE pairs.
 struct QPrepArgs {
   Geom g;
   AttnWs ws;
   int n_q;
   int nq_rows;  // 128-query groups of this call x 128
-  const uint32_t* q;  // bf16 pairs [n_q][H][D/2]
+  const uint4* q;  // bf16 [n_q][H][D]
   const int32_t* q_pos;
 };
 
 template <int D, int TERMS>
 __global__ __launch_bounds__(256) void q_prep_kernel(QPrepArgs A) {
-  constexpr int LPR = D / 2;     // lanes per row
-  constexpr int RPW = 64 / LPR;  // rows per wave
+  constexpr int TPR = 8;          // threads per row
+  constexpr int EPT = D / TPR;    // elements per thread: 16 or 8
   const int H = A.g.n_heads;
-  const int lane = threadIdx.x & 63;
-  const int r = (int)((blockIdx.x * 256 + threadIdx.x) >> 6) * RPW + lane / LPR;  // h * nq_rows + qi
+  const int r = (int)((blockIdx.x * 256 + threadIdx.x) / TPR);  // h * nq_rows + qi
+  const int part = (int)(threadIdx.x % TPR);
   if (r >= H * A.nq_rows) return;  // whole rows only: the reductions stay inside live lanes
-  const int j = lane % LPR;
   const int h = r / A.nq_rows, qi = r % A.nq_rows;
   // rows past n_q read row n_q - 1 (every load in range, no branch around
   // the loads) and are zeroed
   const bool active = qi < A.n_q;
   const int qr = active ? qi : A.n_q - 1;
-  const uint32_t w = A.q[((size_t)qr * H + h) * (D / 2) + j];
-  float cs, sn;
-  rope_cs(A.q_pos[qr], omega_turns(A.g)[j], cs, sn);
-  const float x0 = active ? bf16_lo(w) : 0.f, x1 = active ? bf16_hi(w) : 0.f;
-  float y0 = x0 * cs - x1 * sn;
-  float y1 = x0 * sn + x1 * cs;
-  float am = fmaxf(fabsf(y0), fabsf(y1));
+  const uint4* qp = A.q + ((size_t)qr * H + h) * (D / 8) + part * (EPT / 8);
+  const int32_t p = A.q_pos[qr];
+  const double* turns = omega_turns(A.g) + part * (EPT / 2);
+  float y[EPT];
+  float am = 0.f;
+#pragma unroll
+  for (int c = 0; c < EPT / 8; ++c) {
+    const uint4 w = qp[c];
+    const float xv[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                         bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float cs, sn;
+      rope_cs(p, turns[4 * c + m], cs, sn);
+      const float x0 = active ? xv[2 * m] : 0.f, x1 = active ? xv[2 * m + 1] : 0.f;
+      y[8 * c + 2 * m] = x0 * cs - x1 * sn;
+      y[8 * c + 2 * m + 1] = x0 * sn + x1 * cs;
+      am = fmaxf(am, fmaxf(fabsf(y[8 * c + 2 * m]), fabsf(y[8 * c + 2 * m + 1])));
+    }
+  }
 #pragma unroll
   for (int t = 0; t < TERMS; ++t) {
-    am = group_max<LPR>(am);
+    am = group_max<TPR>(am);
     const int e = am > 0.f ? pow2_exponent(am) : 0;
-    const uint32_t cw = pack2_fp8<false>(clamp448(ldexpf(y0, -e)), clamp448(ldexpf(y1, -e)), 0u);
+    uint32_t wd[EPT / 4];
+    float nm = 0.f;
+#pragma unroll
+    for (int c = 0; c < EPT / 4; ++c) {
+      float* yy = &y[4 * c];
+      // |y| <= 448 * 2^e by the choice of e: no clamping needed
+      const float z0 = ldexpf(yy[0], -e);
+      const uint32_t cw = pack2_fp8<false>(z0, ldexpf(yy[1], -e), __float_as_uint(z0));
+      wd[c] = pack2_fp8<true>(ldexpf(yy[2], -e), ldexpf(yy[3], -e), cw);
+      if (t + 1 < TERMS) {
+        float d0, d1, d2, d3;
+        unpack4_fp8(wd[c], d0, d1, d2, d3);
+        yy[0] -= ldexpf(d0, e);
+        yy[1] -= ldexpf(d1, e);
+        yy[2] -= ldexpf(d2, e);
+        yy[3] -= ldexpf(d3, e);
+        nm = fmaxf(nm, fmaxf(fmaxf(fabsf(yy[0]), fabsf(yy[1])), fmaxf(fabsf(yy[2]), fabsf(yy[3]))));
+      }
+    }
     const size_t row = ((size_t)t * H + h) * A.ws.nq_pad + qi;
-    reinterpret_cast<uint16_t*>(A.ws.qcodes + row * D)[j] = (uint16_t)cw;
-    if (j == 0) A.ws.qexp[row] = e;
-    float d0, d1, d2, d3;
-    unpack4_fp8(cw, d0, d1, d2, d3);
-    y0 -= ldexpf(d0, e);
-    y1 -= ldexpf(d1, e);
-    am = fmaxf(fabsf(y0), fabsf(y1));
+    uint8_t* dst = A.ws.qcodes + row * D + part * EPT;
+    if constexpr (EPT == 16) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    } else {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(wd[0], wd[1]);
+    }
+    if (part == 0) A.ws.qexp[row] = e;
+    am = nm;
   }
 }
 
@@ -685,9 +719,9 @@ hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void*
   P.ws = ws;
   P.n_q = n_q;
   P.nq_rows = nqg * kQG;
-  P.q = (const uint32_t*)q;
+  P.q = (const uint4*)q;
   P.q_pos = q_pos;
-  const int rows = g.n_heads * P.nq_rows, rows_per_block = 4 * (128 / D);
+  const int rows = g.n_heads * P.nq_rows, rows_per_block = 256 / 8;
   const dim3 pgrid((rows + rows_per_block - 1) / rows_per_block);
   if (D == 128) {
     if (ws.terms == 2) hipLaunchKernelGGL((q_prep_kernel<128, 2>), pgrid, dim3(256), 0, s, P);
