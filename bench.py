@@ -9,10 +9,13 @@ position reset: a delta rotation of every cached key by -42 * 757.  The
 cache starts full with its ring head at slot 3,100 (8,888 tokens written).
 
 Prints one JSON line.  `value` is microseconds per step (= per attention call
-with its cache work, resets amortized).  Per-operation times come from
-separate HIP-event-timed loops on the launch stream; `roofline` is the
-attention call (the dominant cost) against the dense FP8 matrix peak.
-`cpu_baseline` times the NumPy float64 oracle on a bounded sample.
+with its cache work, resets amortized), launched eagerly on one stream.  The
+same steps captured once as HIP graphs (the device-side write position makes
+every call capturable) and replayed are reported as
+`components.graph_us_per_step`.  Per-operation times come from separate
+HIP-event-timed loops on the launch stream; `roofline` is the attention call
+(the dominant cost) against the dense FP8 matrix peak.  `cpu_baseline` times
+the NumPy float64 oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -46,7 +49,43 @@ def parse():
     ap.add_argument("--reps", type=int, default=200, help="launches per component loop")
     ap.add_argument("--workgroups", type=int, default=0,
                     help="persistent workgroups per attention call (0 = one per compute unit)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the steps, run one plain copy kernel over this many MiB "
+                         "(fp32 negation, read + write): the reference for HBM byte counters")
     return ap.parse_args()
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attend_757x5788_h12_hbm_traffic.md")
+ATTEND_SOURCES = ["k_attend.hip", "rkv_device.h", "rkv_launch.h"]
+
+
+def attend_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for name in ATTEND_SOURCES:
+        with open(os.path.join(ROOT, "fp8_ring_kv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per attention call from the committed counter record, or None when
+    the record is absent or was taken on different attention sources."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        line = line.strip().strip("`")
+        if line.startswith("sources_sha256:") or line.startswith("hbm_bytes_per_call:"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    if fields.get("sources_sha256") != attend_source_digest() or "hbm_bytes_per_call" not in fields:
+        return None
+    return float(fields["hbm_bytes_per_call"])
 
 
 def to_dev(x):
@@ -112,6 +151,44 @@ def cpu_baseline():
     }
 
 
+def graph_step_ms(args, cache, pool, pos_pool, out, stream):
+    """The bench steps captured once as HIP graphs (one per step of the reset
+    period, the rotation in the first) and replayed, continuing the eager step
+    sequence: the device-side write position makes every call capturable.
+    Average milliseconds per replayed step."""
+    import torch
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for j in range(RESET_EVERY):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                if j == 0:
+                    cache.rotate(0, -RESET_EVERY * CHUNK)
+                q, k, v = pool[j]
+                cache.write(0, k, v, pos_pool[j])
+                cache.attend(0, q, pos_pool[j], out)
+            graphs.append(g)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    first = args.warmup + args.steps
+    for i in range(args.warmup):
+        graphs[(first + i) % RESET_EVERY].replay()
+    first += args.warmup
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(args.steps):
+        graphs[(first + i) % RESET_EVERY].replay()
+    b.record(stream)
+    b.synchronize()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    return a.elapsed_time(b) / args.steps
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -163,6 +240,7 @@ def main():
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
+    # eager launches (one HIP launch per kernel)
     t_host0 = time.perf_counter()
     a.record(stream)
     for i in range(args.steps):
@@ -174,7 +252,17 @@ def main():
     ms_per_step = a.elapsed_time(b) / args.steps
     assert torch.isfinite(out.float()).all()
 
+    if args.copy_mib:
+        # reference kernel for the byte counters: reads and writes copy_mib MiB once
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     comp = {}
+    if not args.no_graph:
+        comp["graph_us_per_step"] = 1e3 * graph_step_ms(args, cache, pool, pos_pool, out, stream)
     if not args.no_components:
         r = args.reps
         q0, k0, v0 = pool[0]
@@ -240,8 +328,8 @@ def main():
         achieved = comp["attend_TFLOPs"]
         res["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2),
                            "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
-                           "kernel": "cache_attend (q_prep + attend + combine)",
+                           "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": recorded_traffic(),
+                           "kernel": "cache_attend call = q_prep_kernel + attend_kernel",
                            "per_launch_flop": ATTN_FLOP,
                            "per_launch_us": round(comp["attend_us"], 3)}
         res["roofline_hbm"] = {
