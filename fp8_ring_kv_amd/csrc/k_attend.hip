@@ -468,12 +468,12 @@ __device__ inline v8i gload32(const uint8_t* p) {
   return r;
 }
 
-// Output of one query row held by a lane: O^T[d][query] for
-// d = 32 b + 8 (r / 4) + 4 gq + r % 4, scaled by inv, as bf16.
-template <int D>
-__device__ inline void store_rows(uint16_t* orow, const v16f (&O)[D / 32], float inv, int gq) {
+// Output of one query row held by a lane, NB 32-dim blocks from orow:
+// O^T[d][query] for d = 32 b + 8 (r / 4) + 4 gq + r % 4, scaled by inv, as bf16.
+template <int NB>
+__device__ inline void store_rows(uint16_t* orow, const v16f (&O)[NB], float inv, int gq) {
 #pragma unroll
-  for (int b = 0; b < D / 32; ++b)
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const uint32_t lo = f32_to_bf16_rne(O[b][4 * g4] * inv) | (f32_to_bf16_rne(O[b][4 * g4 + 1] * inv) << 16);
@@ -483,9 +483,125 @@ __device__ inline void store_rows(uint16_t* orow, const v16f (&O)[D / 32], float
 }
 
 // ---------------------------------------------------------------------------
+// Split-unit partials.  part_o: per segment and wave (qw, gw), the wave's
+// 32 queries x D/2 dims of O / l as fp16, in D/32 chunks of 16 bytes per
+// lane (chunk 2 j + c holds register values 8 c .. 8 c + 7 of block j),
+// chunk-major so that every store and load covers 1 KiB contiguously.
+// part_ml: per segment, query slice qw and lane, the row's (max, sum).
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+constexpr int kSc1 = 16;                 // buffer cache-policy operand: sc1
+constexpr int kRsrcWord3 = 0x00020000;   // raw byte-addressed buffer, 32-bit dwords
+
+struct PartRsrc {
+  __amdgpu_buffer_rsrc_t o, ml;
+  template <int D>
+  __device__ static PartRsrc make(const AttnWs& ws, int segs) {
+    PartRsrc r;
+    r.o = __builtin_amdgcn_make_buffer_rsrc(ws.part_o, 0, segs * 128 * D * 2, kRsrcWord3);
+    r.ml = __builtin_amdgcn_make_buffer_rsrc(ws.part_ml, 0, segs * 4 * 64 * 8, kRsrcWord3);
+    return r;
+  }
+};
+
+__device__ inline int pack_h2(float a, float b) {
+  const h2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(int, v);
+}
+
+// chunk0: index of the lane's first 16-byte chunk (chunk c at chunk0 + 64 c)
+template <int D>
+__device__ inline void store_partial(const PartRsrc& pr, int chunk0, const v16f (&O)[D / 64], float inv) {
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      v4i d;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) d[k] = pack_h2(O[j][8 * c + 2 * k] * inv, O[j][8 * c + 2 * k + 1] * inv);
+      __builtin_amdgcn_raw_buffer_store_b128(d, pr.o, (chunk0 + 64 * (2 * j + c)) * 16, 0, kSc1);
+    }
+}
+
+__device__ inline void store_ml(const PartRsrc& pr, int idx, float m, float l) {
+  const v2i d = {__float_as_int(m), __float_as_int(l)};
+  __builtin_amdgcn_raw_buffer_store_b64(d, pr.ml, idx * 8, 0, kSc1);
+}
+
+// The finisher of unit u: every wave merges its (query slice, dim half) over
+// the unit's segments.  The segment of the workgroup range holding
+// (unit, tile) pair y is floor(((y + 1) G - 1) / W); the next starts at that
+// range's end.  Segments are taken kMB at a time, their loads issued
+// together (a short batch repeats its last segment with weight zero).
+template <int D>
+__device__ __attribute__((always_inline)) inline void merge_unit(const PartRsrc& pr, int u, int count, long long W, int G, int wave,
+                                  int qw, int lane, uint16_t* orow, bool store, float ch, int gq) {
+  constexpr int HB = D / 64, CH = D / 32, kMB = 6;
+  const long long uhi = (long long)(u + 1) * count;
+  long long y = (long long)u * count;
+  float Mu = -INFINITY, Lu = 0.f;
+  v16f acc[HB];
+#pragma unroll
+  for (int j = 0; j < HB; ++j) acc[j] = v16f{};
+  while (y < uhi) {
+    int sg[kMB];
+    bool ok[kMB];
+#pragma unroll
+    for (int k = 0; k < kMB; ++k) {
+      ok[k] = y < uhi;
+      if (ok[k]) {
+        const long long w = ((y + 1) * G - 1) / W;
+        sg[k] = (int)w + u;
+        y = (w + 1) * W / G;
+      } else {
+        sg[k] = sg[k > 0 ? k - 1 : 0];
+      }
+    }
+    v2i ml[kMB];
+    v4i o[kMB][CH];
+#pragma unroll
+    for (int k = 0; k < kMB; ++k) {
+      ml[k] = __builtin_amdgcn_raw_buffer_load_b64(pr.ml, ((sg[k] * 4 + qw) * 64 + lane) * 8, 0, kSc1);
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        o[k][c] = __builtin_amdgcn_raw_buffer_load_b128(pr.o, (((sg[k] * 8 + wave) * CH + c) * 64 + lane) * 16, 0, kSc1);
+    }
+    float Mb = Mu;
+#pragma unroll
+    for (int k = 0; k < kMB; ++k)
+      if (ok[k]) Mb = fmaxf(Mb, __int_as_float(ml[k][0]));
+    const float sc = __builtin_amdgcn_exp2f(Mu - Mb);  // 0 on the first batch
+    Lu *= sc;
+#pragma unroll
+    for (int j = 0; j < HB; ++j) acc[j] *= sc;
+#pragma unroll
+    for (int k = 0; k < kMB; ++k) {
+      const float wk = ok[k] ? __builtin_amdgcn_exp2f(__int_as_float(ml[k][0]) - Mb) * __int_as_float(ml[k][1]) : 0.f;
+      Lu += wk;
+#pragma unroll
+      for (int j = 0; j < HB; ++j)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // (the element goes through a scalar first: a bit_cast of a vector
+            // element directly reads element 0)
+            const int wd = o[k][2 * j + c][e];
+            const h2 v = __builtin_bit_cast(h2, wd);
+            acc[j][8 * c + 2 * e] += wk * (float)v[0];
+            acc[j][8 * c + 2 * e + 1] += wk * (float)v[1];
+          }
+    }
+    Mu = Mb;
+  }
+  if (store) store_rows<HB>(orow, acc, Lu > 0.f ? 1.f / (ch * Lu) : 0.f, gq);
+}
+
+// ---------------------------------------------------------------------------
 template <int D, int TERMS>
 __global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
-  constexpr int KS = D / 64, DB = D / 32;
+  constexpr int KS = D / 64, DB = D / 32, HB = DB / 2, PO_CH = D / 32;
   __shared__ AttnSmem<D> sm;
 
   const Geom& g = A.g;
@@ -611,98 +727,68 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
       }
     }
 
-    // ---- 3. merge the two wave groups through LDS (the tile buffers are free:
-    //         every copy has been waited for) ----
-    __syncthreads();
+    // ---- 3. merge the two wave groups through LDS: afterwards wave (qw, gw)
+    //         holds its 32 queries over the dims of half gw (blocks HB gw ..),
+    //         and both groups hold the merged max and sum ----
+    __syncthreads();  // every wave is done with its tiles (all copies were waited for)
+    v16f keep[HB];
     {
-      constexpr int MS = (DB * 16 + 2) * 64;  // floats per query block
       typedef __attribute__((address_space(3))) float lds_f;
-      lds_f* mb = reinterpret_cast<lds_f*>(kv0) + qw * MS;
-      if (gw == 1) {
+      constexpr int XS = (HB * 16 + 2) * 64;  // floats per wave's exchange block
+      lds_f* mine = reinterpret_cast<lds_f*>(kv0) + wave * XS;
+      const lds_f* theirs = reinterpret_cast<lds_f*>(kv0) + (wave ^ 4) * XS;
 #pragma unroll
-        for (int bb = 0; bb < DB; ++bb)
+      for (int j = 0; j < HB; ++j) {
+        const v16f give = gw ? st.O[j] : st.O[HB + j];
+        keep[j] = gw ? st.O[HB + j] : st.O[j];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mb[(bb * 16 + r) * 64 + lane] = st.O[bb][r];
-        mb[DB * 16 * 64 + lane] = st.m;
-        mb[DB * 16 * 64 + 64 + lane] = st.l;
+        for (int r = 0; r < 16; ++r) mine[(j * 16 + r) * 64 + lane] = give[r];
       }
+      mine[HB * 16 * 64 + lane] = st.m;
+      mine[HB * 16 * 64 + 64 + lane] = st.l;
       __syncthreads();
-      if (gw == 0) {
-        const float m1 = mb[DB * 16 * 64 + lane], l1 = mb[DB * 16 * 64 + 64 + lane];
-        const float M = fmaxf(st.m, m1);  // st.m is finite: group 0 always has a tile
-        const float a0 = __builtin_amdgcn_exp2f(st.m - M), a1 = __builtin_amdgcn_exp2f(m1 - M);
+      const float m1 = theirs[HB * 16 * 64 + lane], l1 = theirs[HB * 16 * 64 + 64 + lane];
+      // a group without tiles has m = -inf, l = 0 and O = 0 (group 0 always has one)
+      const float M = fmaxf(st.m, m1);
+      const float a0 = __builtin_amdgcn_exp2f(st.m - M), a1 = __builtin_amdgcn_exp2f(m1 - M);
 #pragma unroll
-        for (int bb = 0; bb < DB; ++bb)
+      for (int j = 0; j < HB; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) st.O[bb][r] = a0 * st.O[bb][r] + a1 * mb[(bb * 16 + r) * 64 + lane];
-        st.l = a0 * st.l + a1 * l1;
-        st.m = M;
-      }
+        for (int r = 0; r < 16; ++r) keep[j][r] = a0 * keep[j][r] + a1 * theirs[(j * 16 + r) * 64 + lane];
+      st.l = a0 * st.l + a1 * l1;
+      st.m = M;
     }
 
     // ---- 4. whole unit: output; split unit: partial, the last to finish merges ----
     const float Lw = half_swap_add(st.l);
-    uint16_t* orow = A.out + ((size_t)qi * H + h) * D;
+    uint16_t* orow = A.out + ((size_t)qi * H + h) * D + 32 * HB * gw;
     if (t_lo == 0 && t_hi == count) {
-      if (gw == 0 && qi < A.n_q) store_rows<D>(orow, st.O, Lw > 0.f ? 1.f / (ch * Lw) : 0.f, gq);
+      if (qi < A.n_q) store_rows<HB>(orow, keep, Lw > 0.f ? 1.f / (ch * Lw) : 0.f, gq);
     } else {
       // Partial id gi + u is distinct for every (workgroup, unit) pair: ranges
-      // are ordered, so a later workgroup never meets an earlier unit.
+      // are ordered, so a later workgroup never meets an earlier unit.  The
+      // partial is O / l in fp16 (|O / l| <= 448 * 112: the largest e4m3
+      // value code times s_v c_h) plus the row's max and sum in fp32.
+      // Partials travel with sc1 (device-coherent) buffer accesses, the cache
+      // policy of agent-scope relaxed atomics: stores write through and loads
+      // bypass the per-XCD L2s, so no fence has to write back or invalidate a
+      // whole L2.  Each thread's stores complete (vmcnt 0) before the barrier,
+      // and the barrier before the counter update; the finisher reads only
+      // after the counter says every segment has stored.
       const size_t seg = (size_t)gi + u;
-      // Partials travel through device-coherent accesses (relaxed atomics at
-      // agent scope: stores and loads that bypass the per-XCD caches), so no
-      // fence has to write back or invalidate a whole L2.  Each thread's
-      // stores complete (vmcnt 0) before the barrier, and the barrier before
-      // the counter update; the finisher reads only after the counter says
-      // every segment has stored.
-      if (gw == 0) {
-        float* po = A.ws.part_o + (seg * 4 + qw) * (size_t)(DB * 16 * 64);
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            __hip_atomic_store(po + (bb * 16 + r) * 64 + lane, st.O[bb][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        float* pml = A.ws.part_ml + ((seg * 4 + qw) * 64 + lane) * 2;
-        __hip_atomic_store(pml, st.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(pml + 1, Lw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
+      const PartRsrc pr = PartRsrc::make<D>(A.ws, G + U);
+      const float inv = Lw > 0.f ? 1.f / Lw : 0.f;
+      store_partial<D>(pr, (int)(seg * 8 + wave) * PO_CH * 64 + lane, keep, inv);
+      if (gw == 0) store_ml(pr, (int)(seg * 4 + qw) * 64 + lane, st.m, Lw);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (threadIdx.x == 0) {
         const int prev = __hip_atomic_fetch_add(&A.ws.count[u], nk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sm.flag = prev + nk == count;
       }
       __syncthreads();
-      if (sm.flag && gw == 0) {
-        const long long ulo = (long long)u * count, uhi = ulo + count;
-        // segments of unit u, in order: the workgroup range holding tile-unit
-        // y is floor(((y + 1) G - 1) / W); the next segment starts at its end
-        float Mu = -INFINITY;
-        for (long long y = ulo; y < uhi;) {
-          const long long w = ((y + 1) * G - 1) / W;
-          const float* ml = A.ws.part_ml + ((((size_t)w + u) * 4 + qw) * 64 + lane) * 2;
-          Mu = fmaxf(Mu, __hip_atomic_load(ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-          y = (w + 1) * W / G;
-        }
-        v16f acc[DB];
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) acc[bb] = v16f{};
-        float Lu = 0.f;
-        for (long long y = ulo; y < uhi;) {
-          const long long w = ((y + 1) * G - 1) / W;
-          const size_t sid = ((size_t)w + u) * 4 + qw;
-          const float* ml = A.ws.part_ml + (sid * 64 + lane) * 2;
-          const float sc = __builtin_amdgcn_exp2f(__hip_atomic_load(ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - Mu);
-          Lu += sc * __hip_atomic_load(ml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const float* ps = A.ws.part_o + sid * (size_t)(DB * 16 * 64);
-#pragma unroll
-          for (int bb = 0; bb < DB; ++bb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              acc[bb][r] += sc * __hip_atomic_load(ps + (bb * 16 + r) * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          y = (w + 1) * W / G;
-        }
-        if (qi < A.n_q) store_rows<D>(orow, acc, Lu > 0.f ? 1.f / (ch * Lu) : 0.f, gq);
+      if (sm.flag) {
+        merge_unit<D>(pr, u, count, W, G, wave, qw, lane, orow, qi < A.n_q, ch, gq);
         if (threadIdx.x == 0) __hip_atomic_store(&A.ws.count[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }

@@ -99,7 +99,7 @@ Plan make_plan(const rkv_params* p) {
 
   size_t w = g.layer0 + (size_t)p->n_layers * g.layer_bytes;
   // Attention workspace: one partial result per segment of the persistent
-  // grid -- at most units + workgroups of them, each 128 query rows x D fp32
+  // grid -- at most units + workgroups of them, each 128 query rows x D fp16
   // plus (max, sum) per row and half-wave -- and one arrival counter per unit
   // (unit = head x 128-query group).
   const size_t nqg = align_up((size_t)p->max_queries, 128) / 128;
@@ -109,7 +109,7 @@ Plan make_plan(const rkv_params* p) {
   pl.ws.grid = grid;
   pl.ws.terms = p->precision == RKV_PRECISE ? 2 : 1;
   pl.ws_parto = w;
-  w = align_up(w + segs * 128 * D * 4, kAlign);
+  w = align_up(w + segs * 128 * D * 2, kAlign);
   pl.ws_partml = w;
   w = align_up(w + segs * 4 * 64 * 2 * 4, kAlign);
   pl.ws_count = w;
@@ -167,7 +167,7 @@ int ring_cache_create(const rkv_params* p, void* dev_buf, size_t bytes, hipStrea
   c->g = pl.g;
   c->g.base = static_cast<uint8_t*>(dev_buf);
   c->ws = pl.ws;
-  c->ws.part_o = reinterpret_cast<float*>(c->g.base + pl.ws_parto);
+  c->ws.part_o = c->g.base + pl.ws_parto;
   c->ws.part_ml = reinterpret_cast<float*>(c->g.base + pl.ws_partml);
   c->ws.count = reinterpret_cast<int32_t*>(c->g.base + pl.ws_count);
   c->ws.qcodes = c->g.base + pl.ws_qcodes;

@@ -11,8 +11,8 @@ namespace rkv {
 
 // Attention workspace inside the cache buffer (shared by all layers).
 struct AttnWs {
-  float* part_o;   // [units + grid][4 waves][D/32][16][64 lanes] fp32 partial outputs
-  float* part_ml;  // [units + grid][4 waves][64 lanes] fp32 pairs (running max, sum)
+  void* part_o;    // [units + grid][8 waves][D/32 chunks][64 lanes] 16-byte chunks of fp16 O / l
+  float* part_ml;  // [units + grid][4 query slices][64 lanes] fp32 pairs (running max, sum)
   int32_t* count;  // [units] arrival counters of split units (zero between calls)
   uint8_t* qcodes; // [2 terms][H][nq_pad][D] e4m3 codes of the RoPE'd queries
   int32_t* qexp;   // [2 terms][H][nq_pad] power-of-two exponent of each query row and term
