@@ -215,7 +215,7 @@ struct KOp {
 template <int D>
 struct VOp {
   v8i v[D / 32];
-  float sk[2], sv[2];
+  float sk[2];
 };
 
 __device__ inline v8i lds32(const lds_u8* p0, const lds_u8* p1) {
@@ -237,7 +237,8 @@ template <int D>
 struct TileOffsets {
   uint32_t k[D / 64][2];
   uint32_t v[2];
-  uint32_t s;
+  uint32_t s;    // key scale of slot 16 gq + lane % 16 (broadcast per register with DPP)
+  uint32_t sv4;  // value scales of slots 16 gq .. 16 gq + 15 (every lane of the half reads them)
   __device__ TileOffsets(int lane) {
     const int li = lane & 31, gq = lane >> 5;
     const int krow = 16 * ((li >> 2) & 1) + 4 * (li >> 3) + (li & 3);
@@ -248,6 +249,7 @@ struct TileOffsets {
 #pragma unroll
     for (int h = 0; h < 2; ++h) v[h] = (uint32_t)(TileLds<D>::V_OFF + 64 * li + 16 * ((gq + 2 * h) ^ vsw(li)));
     s = (uint32_t)(TileLds<D>::S_OFF + 4 * (16 * gq + (lane & 15)));
+    sv4 = (uint32_t)(TileLds<D>::S_OFF + 256 + 64 * gq);
   }
 };
 
@@ -269,7 +271,6 @@ __device__ inline void read_v(VOp<D>& f, const lds_u8* lb, const TileOffsets<D>&
   for (int sub = 0; sub < 2; ++sub) {
     typedef __attribute__((address_space(3))) const float lds_f;
     f.sk[sub] = *reinterpret_cast<lds_f*>(lb + o.s + 128 * sub);
-    f.sv[sub] = *reinterpret_cast<lds_f*>(lb + o.s + 256 + 128 * sub);
   }
 }
 
@@ -293,16 +294,21 @@ struct WaveState {
 };
 
 // Softmax of one tile's S^T (in registers) and its P V product.
+// The probability scale c_h enters through the exponent: with l2c = log2 c_h,
+// P' = exp2(y - m + l2c) = P c_h, x = P' s_v, and the running sum l
+// accumulates P' (so the output is O / l).  The value scales of the 16
+// slots of a lane's half arrive as four 16-byte LDS reads that every lane of
+// the half shares, one value per accumulator register.
 template <int D, int TERMS>
 __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>& st,
-                                  unsigned long long mask, float kscale, float ch, int lane) {
-  // x = P s_v c_h is formed once and reused; contracting x - e4m3(x) into
-  // fma(P, s_v c_h, -e4m3(x)) would keep the broadcast scale in a register
+                                  unsigned long long mask, float kscale, float l2c, int lane,
+                                  const lds_u8* svp) {
+  // x = P' s_v is formed once and reused; contracting x - e4m3(x) into
+  // fma(P', s_v, -e4m3(x)) would recompute the product
 #pragma clang fp contract(off)
   constexpr int DB = D / 32;
   const int gq = lane >> 5;
   const float tk0 = vf.sk[0] * kscale, tk1 = vf.sk[1] * kscale;
-  const float sv0 = vf.sv[0] * ch, sv1 = vf.sv[1] * ch;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     acc[0][r] *= bcast16(tk0, r);
@@ -331,20 +337,20 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
   }
   // P <= 4 and s_v c_h <= 112, so the conversions below never overflow
   // (fp32 rounding a hair above 448 still rounds to 448 in e4m3).
-  // The empty asm keeps the value-scale broadcasts below the branch above,
-  // next to their multiplies, which then take them as a DPP operand.
-  float svx0 = sv0, svx1 = sv1;
-  asm volatile("" : "+v"(svx0), "+v"(svx1));
+  const float mc = st.m - l2c;
   v8i ph, pl;
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     const int sub = w >> 2, r0 = 4 * (w & 3);
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) const v4f lds_v4f;
+    const v4f sv = *reinterpret_cast<lds_v4f*>(svp + 128 * sub + 4 * r0);
     float x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float p = __builtin_amdgcn_exp2f(acc[sub][r0 + e] - st.m);
+      const float p = __builtin_amdgcn_exp2f(acc[sub][r0 + e] - mc);
       st.l += p;
-      x[e] = p * bcast16(sub ? svx1 : svx0, r0 + e);
+      x[e] = p * sv[e];
     }
     // (the low-half conversion keeps the high half of its third operand,
     // which the high-half conversion overwrites: any register will do)
@@ -666,6 +672,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
     for (int k2 = 0; k2 < kSub; ++k2) vm = max(vm, L.vmax[h * kSub + k2]);
     const float vmaxh = __uint_as_float(vm);
     const float ch = vmaxh > 0.f ? kE4M3Max / (4.f * vmaxh) : 1.f;
+    const float l2c = __log2f(ch);
     TileSrc src;
     src.kbase = L.codes_k + (size_t)h * NP * D;
     src.vbase = L.codes_v + (size_t)h * NT * D * kTile;
@@ -723,7 +730,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
         int rel = sl - a;
         if (rel < 0) rel += N;
         const unsigned long long mask = __ballot(sl < N && rel < nv);
-        softmax_pv<D, TERMS>(sacc, vf, st, mask, A.kscale, ch, lane);
+        softmax_pv<D, TERMS>(sacc, vf, st, mask, A.kscale, l2c, lane, lb + off.sv4);
       }
     }
 
@@ -763,12 +770,12 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
     const float Lw = half_swap_add(st.l);
     uint16_t* orow = A.out + ((size_t)qi * H + h) * D + 32 * HB * gw;
     if (t_lo == 0 && t_hi == count) {
-      if (qi < A.n_q) store_rows<HB>(orow, keep, Lw > 0.f ? 1.f / (ch * Lw) : 0.f, gq);
+      if (qi < A.n_q) store_rows<HB>(orow, keep, Lw > 0.f ? 1.f / Lw : 0.f, gq);
     } else {
       // Partial id gi + u is distinct for every (workgroup, unit) pair: ranges
       // are ordered, so a later workgroup never meets an earlier unit.  The
-      // partial is O / l in fp16 (|O / l| <= 448 * 112: the largest e4m3
-      // value code times s_v c_h) plus the row's max and sum in fp32.
+      // partial is c_h O / l in fp16 (|c_h O / l| <= 448 * 112: the largest
+      // e4m3 value code times s_v c_h) plus the row's max and sum in fp32.
       // Partials travel with sc1 (device-coherent) buffer accesses, the cache
       // policy of agent-scope relaxed atomics: stores write through and loads
       // bypass the per-XCD L2s, so no fence has to write back or invalidate a
@@ -777,7 +784,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
       // after the counter says every segment has stored.
       const size_t seg = (size_t)gi + u;
       const PartRsrc pr = PartRsrc::make<D>(A.ws, G + U);
-      const float inv = Lw > 0.f ? 1.f / Lw : 0.f;
+      const float inv = Lw > 0.f ? ch / Lw : 0.f;
       store_partial<D>(pr, (int)(seg * 8 + wave) * PO_CH * 64 + lane, keep, inv);
       if (gw == 0) store_ml(pr, (int)(seg * 4 + qw) * 64 + lane, st.m, Lw);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
