@@ -132,8 +132,9 @@ struct TileLds {
   static constexpr int COPIES = KC / 2 + 1;  // copy instructions per wave and tile
 };
 
-constexpr int kBufs = 6;   // tile buffers: three pairs (one tile per wave group)
-constexpr int kPairs = kBufs / 2;
+constexpr int kWaves = 4;          // waves per workgroup, one per SIMD
+constexpr int kBufs = 4;           // LDS ring of tile buffers
+constexpr int kLead = kBufs - 1;   // tiles whose copies run ahead of the computed one
 
 template <int D>
 __device__ inline int ksw(int r) {
@@ -489,11 +490,11 @@ __device__ inline void store_rows(uint16_t* orow, const v16f (&O)[NB], float inv
 }
 
 // ---------------------------------------------------------------------------
-// Split-unit partials.  part_o: per segment and wave (qw, gw), the wave's
-// 32 queries x D/2 dims of O / l as fp16, in D/32 chunks of 16 bytes per
-// lane (chunk 2 j + c holds register values 8 c .. 8 c + 7 of block j),
-// chunk-major so that every store and load covers 1 KiB contiguously.
-// part_ml: per segment, query slice qw and lane, the row's (max, sum).
+// Split-unit partials.  part_o: per segment and wave, the wave's 32 queries x
+// D dims of O / l as fp16, in D/16 chunks of 16 bytes per lane (chunk 2 b + c
+// holds register values 8 c .. 8 c + 7 of block b), chunk-major so that every
+// store and load covers 1 KiB contiguously.  part_ml: per segment, wave and
+// lane, the row's (max, sum).
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -506,7 +507,7 @@ struct PartRsrc {
   __device__ static PartRsrc make(const AttnWs& ws, int segs) {
     PartRsrc r;
     r.o = __builtin_amdgcn_make_buffer_rsrc(ws.part_o, 0, segs * 128 * D * 2, kRsrcWord3);
-    r.ml = __builtin_amdgcn_make_buffer_rsrc(ws.part_ml, 0, segs * 4 * 64 * 8, kRsrcWord3);
+    r.ml = __builtin_amdgcn_make_buffer_rsrc(ws.part_ml, 0, segs * kWaves * 64 * 8, kRsrcWord3);
     return r;
   }
 };
@@ -518,15 +519,15 @@ __device__ inline int pack_h2(float a, float b) {
 
 // chunk0: index of the lane's first 16-byte chunk (chunk c at chunk0 + 64 c)
 template <int D>
-__device__ inline void store_partial(const PartRsrc& pr, int chunk0, const v16f (&O)[D / 64], float inv) {
+__device__ inline void store_partial(const PartRsrc& pr, int chunk0, const v16f (&O)[D / 32], float inv) {
 #pragma unroll
-  for (int j = 0; j < D / 64; ++j)
+  for (int b = 0; b < D / 32; ++b)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       v4i d;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) d[k] = pack_h2(O[j][8 * c + 2 * k] * inv, O[j][8 * c + 2 * k + 1] * inv);
-      __builtin_amdgcn_raw_buffer_store_b128(d, pr.o, (chunk0 + 64 * (2 * j + c)) * 16, 0, kSc1);
+      for (int k = 0; k < 4; ++k) d[k] = pack_h2(O[b][8 * c + 2 * k] * inv, O[b][8 * c + 2 * k + 1] * inv);
+      __builtin_amdgcn_raw_buffer_store_b128(d, pr.o, (chunk0 + 64 * (2 * b + c)) * 16, 0, kSc1);
     }
 }
 
@@ -535,21 +536,22 @@ __device__ inline void store_ml(const PartRsrc& pr, int idx, float m, float l) {
   __builtin_amdgcn_raw_buffer_store_b64(d, pr.ml, idx * 8, 0, kSc1);
 }
 
-// The finisher of unit u: every wave merges its (query slice, dim half) over
-// the unit's segments.  The segment of the workgroup range holding
-// (unit, tile) pair y is floor(((y + 1) G - 1) / W); the next starts at that
-// range's end.  Segments are taken kMB at a time, their loads issued
-// together (a short batch repeats its last segment with weight zero).
+// The finisher of unit u: every wave merges its 32 queries over the unit's
+// segments.  The segment of the workgroup range holding (unit, tile) pair y
+// is floor(((y + 1) G - 1) / W); the next starts at that range's end.
+// Segments are taken kMB at a time, their loads issued together (a short
+// batch repeats its last segment with weight zero).
 template <int D>
-__device__ __attribute__((always_inline)) inline void merge_unit(const PartRsrc& pr, int u, int count, long long W, int G, int wave,
-                                  int qw, int lane, uint16_t* orow, bool store, float ch, int gq) {
-  constexpr int HB = D / 64, CH = D / 32, kMB = 6;
+__device__ __attribute__((always_inline)) inline void merge_unit(const PartRsrc& pr, int u, int count, long long W,
+                                                                 int G, int wave, int lane, uint16_t* orow,
+                                                                 bool store, float ch, int gq) {
+  constexpr int DB = D / 32, CH = D / 16, kMB = 2;
   const long long uhi = (long long)(u + 1) * count;
   long long y = (long long)u * count;
   float Mu = -INFINITY, Lu = 0.f;
-  v16f acc[HB];
+  v16f acc[DB];
 #pragma unroll
-  for (int j = 0; j < HB; ++j) acc[j] = v16f{};
+  for (int b = 0; b < DB; ++b) acc[b] = v16f{};
   while (y < uhi) {
     int sg[kMB];
     bool ok[kMB];
@@ -568,10 +570,10 @@ __device__ __attribute__((always_inline)) inline void merge_unit(const PartRsrc&
     v4i o[kMB][CH];
 #pragma unroll
     for (int k = 0; k < kMB; ++k) {
-      ml[k] = __builtin_amdgcn_raw_buffer_load_b64(pr.ml, ((sg[k] * 4 + qw) * 64 + lane) * 8, 0, kSc1);
+      ml[k] = __builtin_amdgcn_raw_buffer_load_b64(pr.ml, ((sg[k] * kWaves + wave) * 64 + lane) * 8, 0, kSc1);
 #pragma unroll
       for (int c = 0; c < CH; ++c)
-        o[k][c] = __builtin_amdgcn_raw_buffer_load_b128(pr.o, (((sg[k] * 8 + wave) * CH + c) * 64 + lane) * 16, 0, kSc1);
+        o[k][c] = __builtin_amdgcn_raw_buffer_load_b128(pr.o, (((sg[k] * kWaves + wave) * CH + c) * 64 + lane) * 16, 0, kSc1);
     }
     float Mb = Mu;
 #pragma unroll
@@ -580,34 +582,50 @@ __device__ __attribute__((always_inline)) inline void merge_unit(const PartRsrc&
     const float sc = __builtin_amdgcn_exp2f(Mu - Mb);  // 0 on the first batch
     Lu *= sc;
 #pragma unroll
-    for (int j = 0; j < HB; ++j) acc[j] *= sc;
+    for (int b = 0; b < DB; ++b) acc[b] *= sc;
 #pragma unroll
     for (int k = 0; k < kMB; ++k) {
       const float wk = ok[k] ? __builtin_amdgcn_exp2f(__int_as_float(ml[k][0]) - Mb) * __int_as_float(ml[k][1]) : 0.f;
       Lu += wk;
 #pragma unroll
-      for (int j = 0; j < HB; ++j)
+      for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             // (the element goes through a scalar first: a bit_cast of a vector
             // element directly reads element 0)
-            const int wd = o[k][2 * j + c][e];
+            const int wd = o[k][2 * b + c][e];
             const h2 v = __builtin_bit_cast(h2, wd);
-            acc[j][8 * c + 2 * e] += wk * (float)v[0];
-            acc[j][8 * c + 2 * e + 1] += wk * (float)v[1];
+            acc[b][8 * c + 2 * e] += wk * (float)v[0];
+            acc[b][8 * c + 2 * e + 1] += wk * (float)v[1];
           }
     }
     Mu = Mb;
   }
-  if (store) store_rows<HB>(orow, acc, Lu > 0.f ? 1.f / (ch * Lu) : 0.f, gq);
+  if (store) store_rows<DB>(orow, acc, Lu > 0.f ? 1.f / (ch * Lu) : 0.f, gq);
 }
 
+// Wait until at most n tiles' copies of this wave are in flight (C copy
+// instructions per tile), then meet the other waves of the workgroup.
+template <int C>
+__device__ inline void wait_tiles_and_barrier(int n) {
+  switch (n) {
+    case 0: wait_copies_and_barrier<0>(); break;
+    case 1: wait_copies_and_barrier<C>(); break;
+    default: wait_copies_and_barrier<2 * C>(); break;
+  }
+}
+static_assert(kLead - 1 <= 2, "wait_tiles_and_barrier covers up to 2 tiles in flight");
+
 // ---------------------------------------------------------------------------
+// Two workgroups per compute unit, 4 waves each: the two waves a SIMD holds
+// belong to different workgroups, whose barriers do not couple them, so one
+// wave's matrix instructions run while the other's softmax uses the vector
+// ALU.
 template <int D, int TERMS>
-__global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
-  constexpr int KS = D / 64, DB = D / 32, HB = DB / 2, PO_CH = D / 32;
+__global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
+  constexpr int KS = D / 64, DB = D / 32;
   __shared__ AttnSmem<D> sm;
 
   const Geom& g = A.g;
@@ -615,12 +633,10 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
   const int G = (int)gridDim.x;
   const int bid = (int)blockIdx.x;
   const int gi = G % 8 == 0 ? (bid & 7) * (G / 8) + (bid >> 3) : bid;  // this workgroup's range
-  // 8 waves: wave w serves queries 32 (w % 4) .. + 31 of the unit and takes
-  // the tiles of parity w / 4 of each pair.  The wave index is uniform per
-  // wave; readfirstlane lets the compiler keep what derives from it in scalar
-  // registers.
+  // wave w serves queries 32 w .. 32 w + 31 of the unit.  The wave index is
+  // uniform per wave; readfirstlane lets the compiler keep what derives from
+  // it in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int gw = wave >> 2, qw = wave & 3;
   const int li = lane & 31, gq = lane >> 5;
 
   const LayerPtrs L = layer_ptrs(g, A.layer);
@@ -636,22 +652,20 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
   }
   const int U = A.nqg * H;
 
-  if (count == 0) {  // empty cache: every output row is zero (wave group 0 writes)
-    if (gw == 0) {
-      for (int u = gi; u < U; u += G) {
-        const int h = u / A.nqg, qi = kQG * (u % A.nqg) + 32 * qw + li;
-        if (qi < A.n_q) {
-          uint4* dst = reinterpret_cast<uint4*>(A.out + ((size_t)qi * H + h) * D + (D / 2) * gq);
+  if (count == 0) {  // empty cache: every output row is zero
+    for (int u = gi; u < U; u += G) {
+      const int h = u / A.nqg, qi = kQG * (u % A.nqg) + 32 * wave + li;
+      if (qi < A.n_q) {
+        uint4* dst = reinterpret_cast<uint4*>(A.out + ((size_t)qi * H + h) * D + (D / 2) * gq);
 #pragma unroll
-          for (int c = 0; c < D / 16; ++c) dst[c] = make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int c = 0; c < D / 16; ++c) dst[c] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
     return;
   }
 
   const TileOffsets<D> off(lane);
-  const CopyOffsets<D> coff(qw, lane);
+  const CopyOffsets<D> coff(wave, lane);
   lds_u8* const kv0 = (lds_u8*)&sm.kv[0][0];  // the tile buffers, as LDS addresses
   constexpr int KVB = TileLds<D>::BYTES;
   constexpr int C = TileLds<D>::COPIES;
@@ -678,18 +692,11 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
     src.vbase = L.codes_v + (size_t)h * NT * D * kTile;
     src.skb = L.scale_k + (size_t)h * NP;
     src.svb = L.scale_v + (size_t)h * NP;
+    auto buf = [&](int tj) { return kv0 + (tj % kBufs) * KVB; };
 
-    // Segment tile j lives in buffer j % kBufs; wave group j % 2 copies it
-    // and computes it.  Copies of the first kPairs - 1 pairs start before
-    // the query loads.
-#pragma unroll
-    for (int j = 0; j < kPairs - 1; ++j) {
-      const int tj = 2 * j + gw;
-      if (tj < nk) copy_tile<D>(kv0 + (tj % kBufs) * KVB, src, tile_of(t_lo + tj), coff, qw, lane);
-    }
-
-    // ---- 1. this wave's 32 prepared queries (B operand of S^T = K Q^T) ----
-    const int qi = kQG * qg + 32 * qw + li;
+    // ---- 1. this wave's 32 prepared queries (B operand of S^T = K Q^T),
+    //         then the copies of the first kLead tiles ----
+    const int qi = kQG * qg + 32 * wave + li;
     v8i qf[TERMS][KS];
     int qs[TERMS];
 #pragma unroll
@@ -699,78 +706,44 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
       for (int ks = 0; ks < KS; ++ks) qf[t][ks] = gload32(A.ws.qcodes + row * D + 64 * ks + 32 * gq);
       qs[t] = 127 + A.ws.qexp[row];
     }
+    for (int tj = 0; tj < kLead && tj < nk; ++tj)
+      copy_tile<D>(buf(tj), src, tile_of(t_lo + tj), coff, wave, lane);
 
-    // ---- 2. the segment's tiles, two at a time (one per wave group) ----
+    // ---- 2. the segment's tiles.  Tile t sits in buffer t % kBufs and is
+    //         read at step t; its copy is issued at step t - kLead, after that
+    //         step's barrier, when the buffer's previous tile (t - kBufs) is no
+    //         longer read ----
     WaveState<D> st;
     st.m = -INFINITY;
     st.l = 0.f;
 #pragma unroll
-    for (int bb = 0; bb < DB; ++bb) st.O[bb] = v16f{};
-    const int npairs = (nk + 1) >> 1;
-    const int last = (nk - 1 - gw) >> 1;  // last pair holding a tile of this group (-1: none)
-    for (int i = 0; i < npairs; ++i) {
-      const int tj = 2 * i + gw;
-      // this wave's copies of the group's next pair may stay in flight
-      if (last - i >= 1) wait_copies_and_barrier<C>();
-      else wait_copies_and_barrier<0>();
-      if (tj < nk) {
-        const lds_u8* lb = kv0 + (tj % kBufs) * KVB;
-        KOp<D> kf;
-        VOp<D> vf;
-        v16f sacc[2];
-        read_k<D>(kf, lb, off);
-        qk<D, TERMS>(sacc, kf, qf, qs);
-        read_v<D>(vf, lb, off);
-        // the buffer of this group's previous tile was last read before the
-        // barrier above: refill it with the group's tile kPairs - 1 pairs on
-        const int tn = tj + 2 * (kPairs - 1);
-        if (tn < nk) copy_tile<D>(kv0 + (tn % kBufs) * KVB, src, tile_of(t_lo + tn), coff, qw, lane);
-        const int T = tile_of(t_lo + tj);
-        const int sl = T * kTile + lane;
-        int rel = sl - a;
-        if (rel < 0) rel += N;
-        const unsigned long long mask = __ballot(sl < N && rel < nv);
-        softmax_pv<D, TERMS>(sacc, vf, st, mask, A.kscale, l2c, lane, lb + off.sv4);
-      }
+    for (int b = 0; b < DB; ++b) st.O[b] = v16f{};
+    for (int j = 0; j < nk; ++j) {
+      // tile j has landed (at most min(nk - j - 1, kLead - 1) later tiles in
+      // flight) and every wave is past step j - 1
+      const int later = min(nk - j - 1, kLead - 1);
+      wait_tiles_and_barrier<C>(later);
+      if (j + kLead < nk) copy_tile<D>(buf(j + kLead), src, tile_of(t_lo + j + kLead), coff, wave, lane);
+      const lds_u8* lb = buf(j);
+      KOp<D> kf;
+      VOp<D> vf;
+      v16f sacc[2];
+      read_k<D>(kf, lb, off);
+      qk<D, TERMS>(sacc, kf, qf, qs);
+      read_v<D>(vf, lb, off);
+      const int T = tile_of(t_lo + j);
+      const int sl = T * kTile + lane;
+      int rel = sl - a;
+      if (rel < 0) rel += N;
+      const unsigned long long mask = __ballot(sl < N && rel < nv);
+      softmax_pv<D, TERMS>(sacc, vf, st, mask, A.kscale, l2c, lane, lb + off.sv4);
     }
 
-    // ---- 3. merge the two wave groups through LDS: afterwards wave (qw, gw)
-    //         holds its 32 queries over the dims of half gw (blocks HB gw ..),
-    //         and both groups hold the merged max and sum ----
-    __syncthreads();  // every wave is done with its tiles (all copies were waited for)
-    v16f keep[HB];
-    {
-      typedef __attribute__((address_space(3))) float lds_f;
-      constexpr int XS = (HB * 16 + 2) * 64;  // floats per wave's exchange block
-      lds_f* mine = reinterpret_cast<lds_f*>(kv0) + wave * XS;
-      const lds_f* theirs = reinterpret_cast<lds_f*>(kv0) + (wave ^ 4) * XS;
-#pragma unroll
-      for (int j = 0; j < HB; ++j) {
-        const v16f give = gw ? st.O[j] : st.O[HB + j];
-        keep[j] = gw ? st.O[HB + j] : st.O[j];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mine[(j * 16 + r) * 64 + lane] = give[r];
-      }
-      mine[HB * 16 * 64 + lane] = st.m;
-      mine[HB * 16 * 64 + 64 + lane] = st.l;
-      __syncthreads();
-      const float m1 = theirs[HB * 16 * 64 + lane], l1 = theirs[HB * 16 * 64 + 64 + lane];
-      // a group without tiles has m = -inf, l = 0 and O = 0 (group 0 always has one)
-      const float M = fmaxf(st.m, m1);
-      const float a0 = __builtin_amdgcn_exp2f(st.m - M), a1 = __builtin_amdgcn_exp2f(m1 - M);
-#pragma unroll
-      for (int j = 0; j < HB; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) keep[j][r] = a0 * keep[j][r] + a1 * theirs[(j * 16 + r) * 64 + lane];
-      st.l = a0 * st.l + a1 * l1;
-      st.m = M;
-    }
-
-    // ---- 4. whole unit: output; split unit: partial, the last to finish merges ----
+    // ---- 3. whole unit: output; split unit: partial, the last to finish merges ----
     const float Lw = half_swap_add(st.l);
-    uint16_t* orow = A.out + ((size_t)qi * H + h) * D + 32 * HB * gw;
+    uint16_t* orow = A.out + ((size_t)qi * H + h) * D;
     if (t_lo == 0 && t_hi == count) {
-      if (qi < A.n_q) store_rows<HB>(orow, keep, Lw > 0.f ? 1.f / Lw : 0.f, gq);
+      if (qi < A.n_q) store_rows<DB>(orow, st.O, Lw > 0.f ? 1.f / Lw : 0.f, gq);
     } else {
       // Partial id gi + u is distinct for every (workgroup, unit) pair: ranges
       // are ordered, so a later workgroup never meets an earlier unit.  The
@@ -782,11 +755,10 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
       // whole L2.  Each thread's stores complete (vmcnt 0) before the barrier,
       // and the barrier before the counter update; the finisher reads only
       // after the counter says every segment has stored.
-      const size_t seg = (size_t)gi + u;
+      const int seg = gi + u;
       const PartRsrc pr = PartRsrc::make<D>(A.ws, G + U);
-      const float inv = Lw > 0.f ? ch / Lw : 0.f;
-      store_partial<D>(pr, (int)(seg * 8 + wave) * PO_CH * 64 + lane, keep, inv);
-      if (gw == 0) store_ml(pr, (int)(seg * 4 + qw) * 64 + lane, st.m, Lw);
+      store_partial<D>(pr, (seg * kWaves + wave) * (D / 16) * 64 + lane, st.O, Lw > 0.f ? ch / Lw : 0.f);
+      store_ml(pr, (seg * kWaves + wave) * 64 + lane, st.m, Lw);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (threadIdx.x == 0) {
@@ -795,7 +767,7 @@ __global__ __launch_bounds__(512, 1) void attend_kernel(AttnArgs A) {
       }
       __syncthreads();
       if (sm.flag) {
-        merge_unit<D>(pr, u, count, W, G, wave, qw, lane, orow, qi < A.n_q, ch, gq);
+        merge_unit<D>(pr, u, count, W, G, wave, lane, orow, qi < A.n_q, ch, gq);
         if (threadIdx.x == 0) __hip_atomic_store(&A.ws.count[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -838,11 +810,11 @@ hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void*
   A.kscale = kLog2e / sqrtf((float)D);
   const dim3 grid(ws.grid);
   if (D == 128) {
-    if (ws.terms == 2) hipLaunchKernelGGL((attend_kernel<128, 2>), grid, dim3(512), 0, s, A);
-    else hipLaunchKernelGGL((attend_kernel<128, 1>), grid, dim3(512), 0, s, A);
+    if (ws.terms == 2) hipLaunchKernelGGL((attend_kernel<128, 2>), grid, dim3(64 * kWaves), 0, s, A);
+    else hipLaunchKernelGGL((attend_kernel<128, 1>), grid, dim3(64 * kWaves), 0, s, A);
   } else {
-    if (ws.terms == 2) hipLaunchKernelGGL((attend_kernel<64, 2>), grid, dim3(512), 0, s, A);
-    else hipLaunchKernelGGL((attend_kernel<64, 1>), grid, dim3(512), 0, s, A);
+    if (ws.terms == 2) hipLaunchKernelGGL((attend_kernel<64, 2>), grid, dim3(64 * kWaves), 0, s, A);
+    else hipLaunchKernelGGL((attend_kernel<64, 1>), grid, dim3(64 * kWaves), 0, s, A);
   }
   return hipGetLastError();
 }

@@ -30,8 +30,8 @@ constexpr int kMaxWorkgroups = 4096;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Compute units of the current device (the persistent attention grid has one
-// workgroup per unit); 256 on MI355X.
+// Compute units of the current device (the persistent attention grid has two
+// workgroups per unit); 256 on MI355X.
 int compute_units() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) == hipSuccess &&
@@ -104,7 +104,7 @@ Plan make_plan(const rkv_params* p) {
   // (unit = head x 128-query group).
   const size_t nqg = align_up((size_t)p->max_queries, 128) / 128;
   const size_t units = nqg * H;
-  const int grid = p->attn_workgroups > 0 ? p->attn_workgroups : compute_units();
+  const int grid = p->attn_workgroups > 0 ? p->attn_workgroups : 2 * compute_units();
   const size_t segs = units + (size_t)grid;
   pl.ws.grid = grid;
   pl.ws.terms = p->precision == RKV_PRECISE ? 2 : 1;
