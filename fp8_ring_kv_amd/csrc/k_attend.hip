@@ -618,6 +618,20 @@ __device__ inline void wait_tiles_and_barrier(int n) {
 }
 static_assert(kLead - 1 <= 2, "wait_tiles_and_barrier covers up to 2 tiles in flight");
 
+// Issue priority from progress: the two waves a SIMD holds come from two
+// workgroups; the SIMD favours the older one, so without this the first
+// workgroup of every compute unit finishes well before the second, which
+// then runs alone, its matrix and vector work no longer overlapped.  A wave
+// that is behind in its segment takes precedence.
+__device__ inline void set_progress_priority(int j, int nk) {
+  switch ((4 * j) / nk) {
+    case 0: __builtin_amdgcn_s_setprio(3); break;
+    case 1: __builtin_amdgcn_s_setprio(2); break;
+    case 2: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Two workgroups per compute unit, 4 waves each: the two waves a SIMD holds
 // belong to different workgroups, whose barriers do not couple them, so one
@@ -723,6 +737,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
       // flight) and every wave is past step j - 1
       const int later = min(nk - j - 1, kLead - 1);
       wait_tiles_and_barrier<C>(later);
+      set_progress_priority(j, nk);
       if (j + kLead < nk) copy_tile<D>(buf(j + kLead), src, tile_of(t_lo + j + kLead), coff, wave, lane);
       const lds_u8* lb = buf(j);
       KOp<D> kf;
@@ -738,6 +753,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
       const unsigned long long mask = __ballot(sl < N && rel < nv);
       softmax_pv<D, TERMS>(sacc, vf, st, mask, A.kscale, l2c, lane, lb + off.sv4);
     }
+
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- 3. whole unit: output; split unit: partial, the last to finish merges ----
     const float Lw = half_swap_add(st.l);
@@ -808,7 +825,18 @@ hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void*
   A.q_pos = q_pos;
   A.out = (uint16_t*)out;
   A.kscale = kLog2e / sqrtf((float)D);
-  const dim3 grid(ws.grid);
+  // With at most one workgroup slot per unit, the grid is a multiple of the
+  // unit count (preferably also of the 8 XCDs), so that every workgroup's
+  // range lies inside one unit: one segment per workgroup, equal splits.
+  int G = ws.grid;
+  const int U = nqg * g.n_heads;
+  if (U <= ws.grid) {
+    int k = ws.grid / U;
+    for (int kk = k; kk >= 1 && U * kk * 8 >= ws.grid * 7; --kk)
+      if (U * kk % 8 == 0) { k = kk; break; }
+    G = U * k;
+  }
+  const dim3 grid(G);
   if (D == 128) {
     if (ws.terms == 2) hipLaunchKernelGGL((attend_kernel<128, 2>), grid, dim3(64 * kWaves), 0, s, A);
     else hipLaunchKernelGGL((attend_kernel<128, 1>), grid, dim3(64 * kWaves), 0, s, A);
