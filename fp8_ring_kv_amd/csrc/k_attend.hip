@@ -6,31 +6,36 @@
 // used as stored (§4.2); the cache is e4m3 with per-head descales and only
 // the queries are quantized per call (§4.3).
 //
+// Two launches per call.  q_prep_kernel applies RoPE to the queries at their
+// positions (angles in double precision) and splits each (query, head) row
+// into one or two e4m3 terms with power-of-two scales, applied exactly by the
+// E8M0 scale operand of the matrix instruction.  attend_kernel then does the
+// attention proper:
+//
 // Work: unit u = (head h, group qg of 128 queries), u = h * nqg + qg; each
 // unit needs `count` 64-slot tiles (the tiles holding valid slots, in cyclic
 // order from the tile of the oldest valid slot).  A persistent grid of G
-// workgroups (two per compute unit) cuts the unit-major list of all
-// units * count (unit, tile) pairs into G equal contiguous ranges, so every
-// workgroup gets the same matrix work to within one tile.  Workgroups are
-// dealt to the 8 XCDs round-robin; ranges are assigned so that each XCD
-// takes a contiguous block of them (one or two heads), keeping their K/V in
-// its L2.
+// 4-wave workgroups, two per compute unit, cuts the unit-major list of all
+// units * count (unit, tile) pairs into G equal contiguous ranges; when the
+// units are fewer than the workgroup slots, G is a multiple of the unit
+// count, so every range lies inside one unit.  Workgroups are dealt to the 8
+// XCDs round-robin; ranges are assigned so that each XCD takes a contiguous
+// block of them (whole heads where possible), keeping their K/V in its L2.
 //
 // A workgroup handles each unit its range meets as one segment:
-//   1. RoPE on the unit's 128 queries (angles in double precision) and their
-//      split into one or two e4m3 terms with power-of-two scales (applied
-//      exactly by the E8M0 scale operand of the matrix instruction), staged
-//      in LDS; wave w keeps queries 32 w .. 32 w + 31 in registers;
-//   2. the tiles stream through two LDS buffers: the K tile, the transposed
-//      V tile and the 128 slot scales of tile i + 1 are copied from global
-//      memory straight into LDS (global_load_lds_dwordx4) while tile i is
-//      computed.  All 4 waves read each tile.  Per tile a wave computes
+//   1. wave w loads the prepared terms of queries 32 w .. 32 w + 31;
+//   2. the tiles stream through a ring of LDS buffers: the K tile, the
+//      transposed V tile and the 128 slot scales of a tile are copied from
+//      global memory straight into LDS (global_load_lds_dwordx4) three
+//      tiles ahead.  Every wave reads every tile.  Per tile a wave computes
 //      S^T = K Q^T with v_mfma_scale_f32_32x32x64_f8f6f4 (rows = slots,
 //      columns = queries: one lane owns one query, so the row max and sum
 //      are in-lane plus one swap with lane ^ 32), applies the per-slot key
 //      scale, updates an online softmax in fp32 (exp2 domain), turns
 //      P * s_v * c_h into one or two e4m3 terms and accumulates
-//      O^T += V^T P^T with the same instruction;
+//      O^T += V^T P^T with the same instruction.  The two waves a SIMD holds
+//      come from different workgroups, so their matrix and vector phases
+//      overlap;
 //   3. a whole unit writes its bf16 output; a unit split between
 //      workgroups writes a partial (O, max, sum) per wave and the last
 //      workgroup to finish its part merges the partials.
