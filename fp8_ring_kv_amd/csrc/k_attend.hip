@@ -26,8 +26,8 @@
 //   1. wave w loads the prepared terms of queries 32 w .. 32 w + 31;
 //   2. the tiles stream through a ring of LDS buffers: the K tile, the
 //      transposed V tile and the 128 slot scales of a tile are copied from
-//      global memory straight into LDS (global_load_lds_dwordx4) three
-//      tiles ahead.  Every wave reads every tile.  Per tile a wave computes
+//      global memory straight into LDS (global_load_lds_dwordx4) one
+//      pair of tiles ahead.  Every wave reads every tile.  Per tile a wave computes
 //      S^T = K Q^T with v_mfma_scale_f32_32x32x64_f8f6f4 (rows = slots,
 //      columns = queries: one lane owns one query, so the row max and sum
 //      are in-lane plus one swap with lane ^ 32), applies the per-slot key
@@ -138,8 +138,7 @@ struct TileLds {
 };
 
 constexpr int kWaves = 4;          // waves per workgroup, one per SIMD
-constexpr int kBufs = 4;           // LDS ring of tile buffers
-constexpr int kLead = kBufs - 1;   // tiles whose copies run ahead of the computed one
+constexpr int kBufs = 4;           // LDS ring of tile buffers: two pairs
 
 template <int D>
 __device__ inline int ksw(int r) {
@@ -611,18 +610,6 @@ __device__ __attribute__((always_inline)) inline void merge_unit(const PartRsrc&
   if (store) store_rows<DB>(orow, acc, Lu > 0.f ? 1.f / (ch * Lu) : 0.f, gq);
 }
 
-// Wait until at most n tiles' copies of this wave are in flight (C copy
-// instructions per tile), then meet the other waves of the workgroup.
-template <int C>
-__device__ inline void wait_tiles_and_barrier(int n) {
-  switch (n) {
-    case 0: wait_copies_and_barrier<0>(); break;
-    case 1: wait_copies_and_barrier<C>(); break;
-    default: wait_copies_and_barrier<2 * C>(); break;
-  }
-}
-static_assert(kLead - 1 <= 2, "wait_tiles_and_barrier covers up to 2 tiles in flight");
-
 // Issue priority from progress: the two waves a SIMD holds come from two
 // workgroups; the SIMD favours the older one, so without this the first
 // workgroup of every compute unit finishes well before the second, which
@@ -714,7 +701,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
     auto buf = [&](int tj) { return kv0 + (tj % kBufs) * KVB; };
 
     // ---- 1. this wave's 32 prepared queries (B operand of S^T = K Q^T),
-    //         then the copies of the first kLead tiles ----
+    //         then the copies of the first pair of tiles ----
     const int qi = kQG * qg + 32 * wave + li;
     v8i qf[TERMS][KS];
     int qs[TERMS];
@@ -725,25 +712,26 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
       for (int ks = 0; ks < KS; ++ks) qf[t][ks] = gload32(A.ws.qcodes + row * D + 64 * ks + 32 * gq);
       qs[t] = 127 + A.ws.qexp[row];
     }
-    for (int tj = 0; tj < kLead && tj < nk; ++tj)
-      copy_tile<D>(buf(tj), src, tile_of(t_lo + tj), coff, wave, lane);
+    for (int tj = 0; tj < 2 && tj < nk; ++tj) copy_tile<D>(buf(tj), src, tile_of(t_lo + tj), coff, wave, lane);
 
-    // ---- 2. the segment's tiles.  Tile t sits in buffer t % kBufs and is
-    //         read at step t; its copy is issued at step t - kLead, after that
-    //         step's barrier, when the buffer's previous tile (t - kBufs) is no
-    //         longer read ----
+    // ---- 2. the segment's tiles, in pairs.  Tile t sits in buffer t % 4.
+    //         One barrier per pair: after it, the pair's tiles have landed and
+    //         the previous pair's buffers are free for the next pair's copies,
+    //         which then have one pair of compute to land ----
     WaveState<D> st;
     st.m = -INFINITY;
     st.l = 0.f;
 #pragma unroll
     for (int b = 0; b < DB; ++b) st.O[b] = v16f{};
     for (int j = 0; j < nk; ++j) {
-      // tile j has landed (at most min(nk - j - 1, kLead - 1) later tiles in
-      // flight) and every wave is past step j - 1
-      const int later = min(nk - j - 1, kLead - 1);
-      wait_tiles_and_barrier<C>(later);
-      set_progress_priority(j, nk);
-      if (j + kLead < nk) copy_tile<D>(buf(j + kLead), src, tile_of(t_lo + j + kLead), coff, wave, lane);
+      if ((j & 1) == 0) {
+        // a new pair of tiles: tiles j, j + 1 have landed and every wave is
+        // done with the previous pair, whose buffers take the next pair
+        wait_copies_and_barrier<0>();
+        set_progress_priority(j, nk);
+        if (j + 2 < nk) copy_tile<D>(buf(j + 2), src, tile_of(t_lo + j + 2), coff, wave, lane);
+        if (j + 3 < nk) copy_tile<D>(buf(j + 3), src, tile_of(t_lo + j + 3), coff, wave, lane);
+      }
       const lds_u8* lb = buf(j);
       KOp<D> kf;
       VOp<D> vf;
