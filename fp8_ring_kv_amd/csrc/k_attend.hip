@@ -365,9 +365,9 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
     if (TERMS == 2) {  // second term: 16 (x - e4m3(x)), descaled by 2^-4
       float d0, d1, d2, d3;
       unpack4_fp8(hw, d0, d1, d2, d3);
-      const float l0 = (x[0] - d0) * 16.f;
-      uint32_t lw = pack2_fp8<false>(l0, (x[1] - d1) * 16.f, __float_as_uint(l0));
-      lw = pack2_fp8<true>((x[2] - d2) * 16.f, (x[3] - d3) * 16.f, lw);
+      const float l0 = x[0] - d0;
+      uint32_t lw = pack2_fp8_div<false>(l0, x[1] - d1, __float_as_uint(l0), 0.0625f);
+      lw = pack2_fp8_div<true>(x[2] - d2, x[3] - d3, lw, 0.0625f);
       pl[w] = (int)lw;
     }
   }

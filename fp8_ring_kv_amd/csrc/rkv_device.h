@@ -106,6 +106,15 @@ __device__ inline uint32_t pack2_fp8(float a, float b, uint32_t old) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
 }
 
+// As pack2_fp8, of a / s and b / s (the conversion divides by its scale
+// operand; for a power of two s the quotient is exact).
+template <bool HI>
+__device__ inline uint32_t pack2_fp8_div(float a, float b, uint32_t old, float s) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, old), a, b, s, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // Four e4m3fn codes of one dword -> four floats.
 __device__ inline void unpack4_fp8(uint32_t w, float& a, float& b, float& c, float& d) {
   auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
