@@ -278,17 +278,23 @@ hipError_t launch_write(const Geom& g, int layer, const void* k, const void* v, 
 // Delta rotation.  One (slot, head) key row per D/16 lanes (16 codes each);
 // rows are visited in memory order (head-major, slot-minor) so each
 // workgroup streams a contiguous block of codes_k.  Only slots of the valid
-// cyclic range [head - n_valid, head) are touched.
+// cyclic range [head - n_valid, head) are touched.  Each thread takes kRPT
+// rows, 256 / (D/16) rows apart, and issues all their loads before any
+// arithmetic: more bytes in flight than one row per thread, which a
+// streaming pass over HBM needs to cover the memory latency.  The code rows
+// are read and written with the nontemporal hint (a one-pass stream).
 struct RotTable {
   float c[kMaxHalfDim];
   float s[kMaxHalfDim];
 };
+constexpr int kRPT = 4;  // rows per thread
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 
 template <int D>
 __global__ __launch_bounds__(256) void rotate_kernel(Geom g, int layer_lo, int32_t delta,
                                                     RotTable tab) {
   constexpr int LPR = D / 16;
-  constexpr int RPW = 256 / LPR;
+  constexpr int RPW = 256 / LPR;  // rows per workgroup and pass
   __shared__ float cs[D / 2], sn[D / 2];
   if (threadIdx.x < D / 2) {
     cs[threadIdx.x] = tab.c[threadIdx.x];
@@ -301,50 +307,63 @@ __global__ __launch_bounds__(256) void rotate_kernel(Geom g, int layer_lo, int32
   const int head = L.state[0], nv = L.state[1];
   int a = head - nv;
   if (a < 0) a += N;
-  const int row = blockIdx.x * RPW + threadIdx.x / LPR;
   const int lane = threadIdx.x % LPR;
-  const int h = row / NP, slot = row % NP;
-  int rel = slot - a;
-  if (rel < 0) rel += N;
-  const bool valid = h < g.n_heads && slot < N && rel < nv;
 
-  uint4 w = make_uint4(0u, 0u, 0u, 0u);
-  float sc = 0.f;
-  const size_t r = (size_t)h * NP + slot;
-  if (valid) {
-    w = *reinterpret_cast<const uint4*>(L.codes_k + r * D + 16 * lane);
-    sc = L.scale_k[r];
-  }
-  float x[16];
-  unpack4_fp8(w.x, x[0], x[1], x[2], x[3]);
-  unpack4_fp8(w.y, x[4], x[5], x[6], x[7]);
-  unpack4_fp8(w.z, x[8], x[9], x[10], x[11]);
-  unpack4_fp8(w.w, x[12], x[13], x[14], x[15]);
-  float y[16];
-  float am = 0.f;
+  uint4 w[kRPT];
+  float sc[kRPT];
+  size_t r[kRPT];
+  int slot[kRPT];
+  bool valid[kRPT];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const float c = cs[8 * lane + m], s = sn[8 * lane + m];
-    const float x0 = x[2 * m] * sc, x1 = x[2 * m + 1] * sc;
-    y[2 * m] = x0 * c - x1 * s;
-    y[2 * m + 1] = x0 * s + x1 * c;
-    am = fmaxf(am, fmaxf(fabsf(y[2 * m]), fabsf(y[2 * m + 1])));
+  for (int k = 0; k < kRPT; ++k) {
+    const int row = (blockIdx.x * kRPT + k) * RPW + threadIdx.x / LPR;
+    const int h = row / NP;
+    slot[k] = row % NP;
+    int rel = slot[k] - a;
+    if (rel < 0) rel += N;
+    valid[k] = h < g.n_heads && slot[k] < N && rel < nv;
+    r[k] = (size_t)h * NP + slot[k];
+    w[k] = make_uint4(0u, 0u, 0u, 0u);
+    sc[k] = 0.f;
+    if (valid[k]) {
+      const u4v t = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(L.codes_k + r[k] * D + 16 * lane));
+      w[k] = make_uint4(t[0], t[1], t[2], t[3]);
+      sc[k] = L.scale_k[r[k]];
+    }
   }
-  am = group_max<LPR>(am);
-  const float sn2 = am * g.margin / kE4M3Max;
-  const float rn = sn2 > 0.f ? 1.f / sn2 : 0.f;
-  uint4 o;
-  uint32_t* ow = &o.x;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t t = pack2_fp8<false>(quant_mul(y[4 * q], rn), quant_mul(y[4 * q + 1], rn), 0u);
-    ow[q] = pack2_fp8<true>(quant_mul(y[4 * q + 2], rn), quant_mul(y[4 * q + 3], rn), t);
-  }
-  if (valid) {
-    *reinterpret_cast<uint4*>(L.codes_k + r * D + 16 * lane) = o;
-    if (lane == 0) {
-      L.scale_k[r] = sn2;
-      if (h == 0) L.slot_pos[slot] += delta;
+  for (int k = 0; k < kRPT; ++k) {
+    float x[16];
+    unpack4_fp8(w[k].x, x[0], x[1], x[2], x[3]);
+    unpack4_fp8(w[k].y, x[4], x[5], x[6], x[7]);
+    unpack4_fp8(w[k].z, x[8], x[9], x[10], x[11]);
+    unpack4_fp8(w[k].w, x[12], x[13], x[14], x[15]);
+    float y[16];
+    float am = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const float c = cs[8 * lane + m], s = sn[8 * lane + m];
+      const float x0 = x[2 * m] * sc[k], x1 = x[2 * m + 1] * sc[k];
+      y[2 * m] = x0 * c - x1 * s;
+      y[2 * m + 1] = x0 * s + x1 * c;
+      am = fmaxf(am, fmaxf(fabsf(y[2 * m]), fabsf(y[2 * m + 1])));
+    }
+    am = group_max<LPR>(am);
+    const float sn2 = am * g.margin / kE4M3Max;
+    const float rn = sn2 > 0.f ? 1.f / sn2 : 0.f;
+    uint4 o;
+    uint32_t* ow = &o.x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t t = pack2_fp8<false>(quant_mul(y[4 * q], rn), quant_mul(y[4 * q + 1], rn), 0u);
+      ow[q] = pack2_fp8<true>(quant_mul(y[4 * q + 2], rn), quant_mul(y[4 * q + 3], rn), t);
+    }
+    if (valid[k]) {
+      __builtin_nontemporal_store(u4v{o.x, o.y, o.z, o.w}, reinterpret_cast<u4v*>(L.codes_k + r[k] * D + 16 * lane));
+      if (lane == 0) {
+        L.scale_k[r[k]] = sn2;
+        if (r[k] < (size_t)NP) L.slot_pos[slot[k]] += delta;  // head 0 rows
+      }
     }
   }
 }
@@ -358,9 +377,9 @@ hipError_t launch_rotate(const Geom& g, int layer_lo, int layer_hi, int32_t delt
     tab.s[j] = sinv[j];
   }
   const int lpr = g.head_dim / 16;
-  const int rpw = 256 / lpr;
+  const long long rows_per_wg = (long long)(256 / lpr) * kRPT;
   const long long rows = (long long)g.n_heads * g.n_pad;
-  dim3 grid((unsigned)((rows + rpw - 1) / rpw), layer_hi - layer_lo);
+  dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg), layer_hi - layer_lo);
   if (g.head_dim == 128)
     hipLaunchKernelGGL(rotate_kernel<128>, grid, dim3(256), 0, s, g, layer_lo, delta, tab);
   else
