@@ -47,6 +47,7 @@ class rkv_params(ctypes.Structure):
         ("rope_base", ctypes.c_float),
         ("scale_margin", ctypes.c_float),
         ("attn_workgroups", ctypes.c_int32),
+        ("attn_merge_wait_us", ctypes.c_int32),
     ]
 
 
@@ -183,9 +184,10 @@ class RingCache:
 
     def __init__(self, n_layers: int, n_slots: int, n_heads: int, head_dim: int, max_queries: int,
                  precision: int = RKV_PRECISE, rope_base: float = 10000.0, scale_margin: float = 1.0,
-                 device: str | torch.device = "cuda", stream=None, attn_workgroups: int = 0):
+                 device: str | torch.device = "cuda", stream=None, attn_workgroups: int = 0,
+                 attn_merge_wait_us: int = -1):
         self.params = rkv_params(n_layers, n_slots, n_heads, head_dim, max_queries, precision,
-                                 rope_base, scale_margin, attn_workgroups)
+                                 rope_base, scale_margin, attn_workgroups, attn_merge_wait_us)
         nbytes = ring_cache_bytes(self.params)
         if nbytes == 0:
             raise RkvError(RKV_EINVAL, "ring_cache_bytes")

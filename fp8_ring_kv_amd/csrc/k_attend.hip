@@ -409,6 +409,10 @@ __global__ __launch_bounds__(256) void q_prep_kernel(QPrepArgs A) {
   const int H = A.g.n_heads;
   const int r = (int)((blockIdx.x * 256 + threadIdx.x) / TPR);  // h * nq_rows + qi
   const int part = (int)(threadIdx.x % TPR);
+  {  // the arrival words of this call's units start at zero
+    const int gt = (int)(blockIdx.x * 256 + threadIdx.x);
+    if (gt < H * (A.nq_rows / 128)) A.ws.sync[(size_t)gt * kSyncStride] = 0ull;
+  }
   if (r >= H * A.nq_rows) return;  // whole rows only: the reductions stay inside live lanes
   const int h = r / A.nq_rows, qi = r % A.nq_rows;
   // rows past n_q read row n_q - 1 (every load in range, no branch around
@@ -540,44 +544,44 @@ __device__ inline void store_ml(const PartRsrc& pr, int idx, float m, float l) {
   __builtin_amdgcn_raw_buffer_store_b64(d, pr.ml, idx * 8, 0, kSc1);
 }
 
-// The finisher of unit u: every wave merges its 32 queries over the unit's
-// segments.  The segment of the workgroup range holding (unit, tile) pair y
-// is floor(((y + 1) G - 1) / W); the next starts at that range's end.
-// Segments are taken kMB at a time, their loads issued together (a short
-// batch repeats its last segment with weight zero).
+// Merge of one output block of split unit u: query slice qs (32 queries) x
+// dim block b (32 dims), over all the unit's segments in segment order, by
+// one wave (the same arithmetic whichever wave and workgroup does it).  The
+// segment of the workgroup range holding (unit, tile) pair y is
+// floor(((y + 1) G - 1) / W); the next starts at that range's end.
+// Segments are taken kMB at a time, their loads issued together; a short
+// batch points its spare loads past the end of the buffer, which returns
+// zeros without a memory access.
 template <int D>
-__device__ __attribute__((always_inline)) inline void merge_unit(const PartRsrc& pr, int u, int count, long long W,
-                                                                 int G, int wave, int lane, uint16_t* orow,
-                                                                 bool store, float ch, int gq) {
-  constexpr int DB = D / 32, CH = D / 16, kMB = 2;
+__device__ __attribute__((always_inline)) inline void merge_block(const PartRsrc& pr, int u, int count, long long W,
+                                                                  int G, int qs, int b, int lane, uint16_t* orow,
+                                                                  bool store, float ch, int gq) {
+  constexpr int CH = D / 16, kMB = 8;
+  constexpr int kPast = 0x40000000;  // a byte offset beyond any partial buffer
   const long long uhi = (long long)(u + 1) * count;
   long long y = (long long)u * count;
   float Mu = -INFINITY, Lu = 0.f;
-  v16f acc[DB];
-#pragma unroll
-  for (int b = 0; b < DB; ++b) acc[b] = v16f{};
+  v16f acc = v16f{};
   while (y < uhi) {
     int sg[kMB];
     bool ok[kMB];
 #pragma unroll
     for (int k = 0; k < kMB; ++k) {
-      ok[k] = y < uhi;
-      if (ok[k]) {
-        const long long w = ((y + 1) * G - 1) / W;
-        sg[k] = (int)w + u;
-        y = (w + 1) * W / G;
-      } else {
-        sg[k] = sg[k > 0 ? k - 1 : 0];
-      }
+      const long long w = y < uhi ? ((y + 1) * G - 1) / W : -1;
+      ok[k] = w >= 0;
+      sg[k] = (int)w + u;
+      if (ok[k]) y = (w + 1) * W / G;
     }
     v2i ml[kMB];
-    v4i o[kMB][CH];
+    v4i o[kMB][2];
 #pragma unroll
     for (int k = 0; k < kMB; ++k) {
-      ml[k] = __builtin_amdgcn_raw_buffer_load_b64(pr.ml, ((sg[k] * kWaves + wave) * 64 + lane) * 8, 0, kSc1);
+      const int base = sg[k] * kWaves + qs;
+      ml[k] = __builtin_amdgcn_raw_buffer_load_b64(pr.ml, ok[k] ? (base * 64 + lane) * 8 : kPast, 0, kSc1);
 #pragma unroll
-      for (int c = 0; c < CH; ++c)
-        o[k][c] = __builtin_amdgcn_raw_buffer_load_b128(pr.o, (((sg[k] * kWaves + wave) * CH + c) * 64 + lane) * 16, 0, kSc1);
+      for (int c = 0; c < 2; ++c)
+        o[k][c] = __builtin_amdgcn_raw_buffer_load_b128(pr.o, ok[k] ? ((base * CH + 2 * b + c) * 64 + lane) * 16 : kPast,
+                                                        0, kSc1);
     }
     float Mb = Mu;
 #pragma unroll
@@ -585,29 +589,46 @@ __device__ __attribute__((always_inline)) inline void merge_unit(const PartRsrc&
       if (ok[k]) Mb = fmaxf(Mb, __int_as_float(ml[k][0]));
     const float sc = __builtin_amdgcn_exp2f(Mu - Mb);  // 0 on the first batch
     Lu *= sc;
-#pragma unroll
-    for (int b = 0; b < DB; ++b) acc[b] *= sc;
+    acc *= sc;
 #pragma unroll
     for (int k = 0; k < kMB; ++k) {
       const float wk = ok[k] ? __builtin_amdgcn_exp2f(__int_as_float(ml[k][0]) - Mb) * __int_as_float(ml[k][1]) : 0.f;
       Lu += wk;
 #pragma unroll
-      for (int b = 0; b < DB; ++b)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // (the element goes through a scalar first: a bit_cast of a vector
-            // element directly reads element 0)
-            const int wd = o[k][2 * b + c][e];
-            const h2 v = __builtin_bit_cast(h2, wd);
-            acc[b][8 * c + 2 * e] += wk * (float)v[0];
-            acc[b][8 * c + 2 * e + 1] += wk * (float)v[1];
-          }
+        for (int e = 0; e < 4; ++e) {
+          // (the element goes through a scalar first: a bit_cast of a vector
+          // element directly reads element 0)
+          const int wd = o[k][c][e];
+          const h2 v = __builtin_bit_cast(h2, wd);
+          acc[8 * c + 2 * e] += wk * (float)v[0];
+          acc[8 * c + 2 * e + 1] += wk * (float)v[1];
+        }
     }
     Mu = Mb;
   }
-  if (store) store_rows<DB>(orow, acc, Lu > 0.f ? 1.f / (ch * Lu) : 0.f, gq);
+  const v16f a1[1] = {acc};
+  if (store) store_rows<1>(orow + 32 * b, a1, Lu > 0.f ? 1.f / (ch * Lu) : 0.f, gq);
+}
+
+constexpr int kLastArrival = 1 << 30;                  // flag beside a block mask
+template <int D>
+constexpr uint32_t kAllBlocks = (1u << (4 * (D / 32))) - 1u;  // 4 query slices x D/32 dim blocks
+
+// Share of split unit u's output blocks that the workgroup with range gi
+// merges when the unit is where its range ends: block j goes to the
+// workgroup ranges spanning the unit round-robin, j = (gi - first) mod
+// their number.  (Ranges that are empty when W < G take no part: their
+// blocks fall to the last arrival.)
+template <int D>
+__device__ inline uint32_t merge_share(int u, int count, long long W, int G, int gi) {
+  const long long w_first = (((long long)u * count + 1) * G - 1) / W;
+  const long long w_last = (((long long)(u + 1) * count) * G - 1) / W;
+  const int nseg = (int)(w_last - w_first + 1), sidx = gi - (int)w_first;
+  uint32_t m = 0u;
+  for (int j = sidx; j < 4 * (D / 32); j += nseg) m |= 1u << j;
+  return m;
 }
 
 // Issue priority from progress: the two waves a SIMD holds come from two
@@ -678,6 +699,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
   const long long W = (long long)U * count;
   const long long r_lo = (long long)gi * W / G, r_hi = (long long)(gi + 1) * W / G;
   auto tile_of = [&](int kk) { const int T = T0 + kk; return T >= NT ? T - NT : T; };
+  int fin[2], nfin = 0;  // split units with output blocks for this workgroup to merge,
+  int fin_blocks[2];     // ... those blocks, with kLastArrival if it was their last arrival
 
   for (long long x = r_lo; x < r_hi;) {
     const int u = (int)(x / count);
@@ -771,17 +794,77 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
       store_ml(pr, (seg * kWaves + wave) * 64 + lane, st.m, Lw);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      // Arrival: one atomic add of (tiles | committed blocks << 32) on the
+      // unit's word.  A workgroup whose range ends in this unit commits to
+      // merge its share of the unit's output blocks after the loop; the
+      // arrival that completes the tile count takes every block not
+      // committed by another workgroup.
+      const bool waits = x >= r_hi;
       if (threadIdx.x == 0) {
-        const int prev = __hip_atomic_fetch_add(&A.ws.count[u], nk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm.flag = prev + nk == count;
+        const uint32_t commit = waits ? merge_share<D>(u, count, W, G, gi) : 0u;
+        const unsigned long long old = __hip_atomic_fetch_add(
+            &A.ws.sync[(size_t)u * kSyncStride], (unsigned long long)nk | ((unsigned long long)commit << 32),
+            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = (int)(uint32_t)old + nk == count;
+        sm.flag = last ? kLastArrival | (int)(kAllBlocks<D> & ~(uint32_t)(old >> 32)) : (int)commit;
       }
       __syncthreads();
-      if (sm.flag) {
-        merge_unit<D>(pr, u, count, W, G, wave, lane, orow, qi < A.n_q, ch, gq);
-        if (threadIdx.x == 0) __hip_atomic_store(&A.ws.count[u], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (sm.flag != 0) {  // blocks of this unit to merge after the loop
+        fin[nfin] = u;
+        fin_blocks[nfin++] = sm.flag;
       }
     }
     __syncthreads();  // LDS is reused by the next segment
+  }
+
+  // ---- 4. merges of split units.  The last arrival merges its blocks at
+  //         once.  A committed workgroup waits (bounded) for the unit's tile
+  //         count to complete, then merges its committed blocks; if its wait
+  //         runs out it withdraws the commitment with a second atomic add,
+  //         and merges them all the same if that add shows the count
+  //         complete (the last arrival then excluded them), else leaves them
+  //         to the last arrival.  Each block is merged exactly once, with the
+  //         same arithmetic whoever merges it. ----
+  for (int f = 0; f < nfin; ++f) {
+    const int u = fin[f];
+    int blocks = fin_blocks[f];
+    if (!(blocks & kLastArrival)) {
+      if (threadIdx.x == 0) {
+        unsigned long long* const word = &A.ws.sync[(size_t)u * kSyncStride];
+        bool ready = false;
+        const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+        for (int it = 0; it < (1 << 16); ++it) {
+          ready = (int)(uint32_t)__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == count;
+          if (ready || __builtin_amdgcn_s_memrealtime() - t0 >= (unsigned long long)A.ws.wait_ticks) break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+        if (!ready) {
+          const unsigned long long old = __hip_atomic_fetch_sub(word, (unsigned long long)(uint32_t)blocks << 32,
+                                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((int)(uint32_t)old != count) blocks = 0;
+        }
+        sm.flag = blocks;
+      }
+      __syncthreads();
+      blocks = sm.flag;
+      __syncthreads();  // sm.flag is rewritten for the next unit
+    }
+    const int h = u / A.nqg, qg = u % A.nqg;
+    uint32_t vm = 0u;
+#pragma unroll
+    for (int k2 = 0; k2 < kSub; ++k2) vm = max(vm, L.vmax[h * kSub + k2]);
+    const float vmaxh = __uint_as_float(vm);
+    const float ch = vmaxh > 0.f ? kE4M3Max / (4.f * vmaxh) : 1.f;
+    const PartRsrc pr = PartRsrc::make<D>(A.ws, G + U);
+    uint32_t bits = (uint32_t)blocks & kAllBlocks<D>;
+    for (int n = 0; bits; ++n) {  // the n-th block goes to wave n % 4
+      const int j = __builtin_ctz(bits);
+      bits &= bits - 1;
+      if (n % kWaves == wave) {
+        const int qs = j / DB, b = j % DB, qi = kQG * qg + 32 * qs + li;
+        merge_block<D>(pr, u, count, W, G, qs, b, lane, A.out + ((size_t)qi * H + h) * D, qi < A.n_q, ch, gq);
+      }
+    }
   }
 }
 

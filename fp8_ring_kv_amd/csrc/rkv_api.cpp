@@ -43,7 +43,7 @@ int compute_units() {
 struct Plan {
   rkv::Geom g;
   rkv::AttnWs ws;  // pointers filled relative to base 0 (offsets) until create
-  size_t ws_parto, ws_partml, ws_count, ws_qcodes, ws_qexp;
+  size_t ws_parto, ws_partml, ws_sync, ws_qcodes, ws_qexp;
   size_t total;
 };
 
@@ -63,6 +63,8 @@ bool params_ok(const rkv_params* p, std::string* why) {
     return *why = "scale_margin must be in (0, 64]", false;
   if (p->attn_workgroups < 0 || p->attn_workgroups > kMaxWorkgroups)
     return *why = "attn_workgroups out of range [0, 4096]", false;
+  if (p->attn_merge_wait_us < -1 || p->attn_merge_wait_us > 10000)
+    return *why = "attn_merge_wait_us out of range [-1, 10000]", false;
   return true;
 }
 
@@ -100,20 +102,22 @@ Plan make_plan(const rkv_params* p) {
   size_t w = g.layer0 + (size_t)p->n_layers * g.layer_bytes;
   // Attention workspace: one partial result per segment of the persistent
   // grid -- at most units + workgroups of them, each 128 query rows x D fp16
-  // plus (max, sum) per row and half-wave -- and one arrival counter per unit
-  // (unit = head x 128-query group).
+  // plus (max, sum) per row and half-wave -- and per unit (head x 128-query
+  // group) an arrival word on a line of its own.
   const size_t nqg = align_up((size_t)p->max_queries, 128) / 128;
   const size_t units = nqg * H;
   const int grid = p->attn_workgroups > 0 ? p->attn_workgroups : 2 * compute_units();
   const size_t segs = units + (size_t)grid;
   pl.ws.grid = grid;
   pl.ws.terms = p->precision == RKV_PRECISE ? 2 : 1;
+  // the device real-time clock counts at 100 MHz
+  pl.ws.wait_ticks = 100 * (p->attn_merge_wait_us < 0 ? 50 : p->attn_merge_wait_us);
   pl.ws_parto = w;
   w = align_up(w + segs * 128 * D * 2, kAlign);
   pl.ws_partml = w;
   w = align_up(w + segs * 4 * 64 * 2 * 4, kAlign);
-  pl.ws_count = w;
-  w = align_up(w + units * 4, kAlign);
+  pl.ws_sync = w;
+  w = align_up(w + units * rkv::kSyncStride * 8, kAlign);
   // prepared queries: two e4m3 terms per element and an exponent per row and term
   pl.ws.nq_pad = (int32_t)(nqg * 128);
   pl.ws_qcodes = w;
@@ -169,7 +173,7 @@ int ring_cache_create(const rkv_params* p, void* dev_buf, size_t bytes, hipStrea
   c->ws = pl.ws;
   c->ws.part_o = c->g.base + pl.ws_parto;
   c->ws.part_ml = reinterpret_cast<float*>(c->g.base + pl.ws_partml);
-  c->ws.count = reinterpret_cast<int32_t*>(c->g.base + pl.ws_count);
+  c->ws.sync = reinterpret_cast<unsigned long long*>(c->g.base + pl.ws_sync);
   c->ws.qcodes = c->g.base + pl.ws_qcodes;
   c->ws.qexp = reinterpret_cast<int32_t*>(c->g.base + pl.ws_qexp);
   c->bytes = pl.total;

@@ -10,15 +10,21 @@
 namespace rkv {
 
 // Attention workspace inside the cache buffer (shared by all layers).
+constexpr int kSyncStride = 16;  // 64-bit words between units' arrival words
+
 struct AttnWs {
-  void* part_o;    // [units + grid][8 waves][D/32 chunks][64 lanes] 16-byte chunks of fp16 O / l
+  void* part_o;    // [units + grid][4 query slices][D/16 chunks][64 lanes] 16-byte chunks of fp16 c_h O / l
   float* part_ml;  // [units + grid][4 query slices][64 lanes] fp32 pairs (running max, sum)
-  int32_t* count;  // [units] arrival counters of split units (zero between calls)
+  // [units][kSyncStride] per split unit, in the first word of its own 128-byte
+  // line: tiles arrived (low half) | output blocks committed to a merge
+  // (high half); zeroed for the call's units by q_prep_kernel
+  unsigned long long* sync;
   uint8_t* qcodes; // [2 terms][H][nq_pad][D] e4m3 codes of the RoPE'd queries
   int32_t* qexp;   // [2 terms][H][nq_pad] power-of-two exponent of each query row and term
   int32_t nq_pad;  // max_queries rounded up to 128
   int32_t grid;    // persistent workgroups
   int32_t terms;   // 2 = precise, 1 = fast
+  int32_t wait_ticks;  // bound on a merge wait, in ticks of the 100 MHz real-time clock
 };
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);

@@ -70,7 +70,14 @@ typedef struct {
   float rope_base;     /* RoPE base, omega_j = base^(-2j/D); 10000 */
   float scale_margin;  /* scale s = margin * amax / 448; 1.0 */
   int32_t attn_workgroups; /* persistent workgroups of one attention call
-                              (1 .. 4096); 0 = one per compute unit */
+                              (1 .. 4096); 0 = two per compute unit */
+  int32_t attn_merge_wait_us; /* longest wait of a workgroup for the last
+                              arrival on a split unit before it leaves its
+                              share of the merge to that arrival (0 .. 10000
+                              microseconds; -1 = the default, 50).  0 leaves
+                              every merge whose partials are not complete on
+                              arrival to the last arrival; results do not
+                              depend on this value */
 } rkv_params;
 
 /* Byte offsets into the cache buffer for one layer.  Layout (N_pad = N

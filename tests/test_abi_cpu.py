@@ -44,7 +44,8 @@ def test_single_hip_runtime_in_process():
 
 def params(**kw):
     base = dict(n_layers=1, n_slots=5788, n_heads=12, head_dim=128, max_queries=757,
-                precision=rkv.RKV_PRECISE, rope_base=10000.0, scale_margin=1.0, attn_workgroups=0)
+                precision=rkv.RKV_PRECISE, rope_base=10000.0, scale_margin=1.0, attn_workgroups=0,
+                attn_merge_wait_us=-1)
     base.update(kw)
     return rkv.rkv_params(**base)
 
@@ -65,6 +66,7 @@ def test_bytes_cover_the_layout():
     ("head_dim", 96), ("head_dim", 256), ("max_queries", 0), ("precision", 7),
     ("rope_base", 1.0), ("rope_base", float("inf")), ("scale_margin", 0.0),
     ("attn_workgroups", -1), ("attn_workgroups", 4097),
+    ("attn_merge_wait_us", -2), ("attn_merge_wait_us", 10001),
 ])
 def test_invalid_params_give_zero_bytes_and_einval(field, value):
     p = params(**{field: value})

@@ -225,6 +225,43 @@ def test_stress_partial_fill_sessions():
             gate(f"stress write {w} (valid {st.n_valid})", out[rows][:, heads], ex, oatt.sigma_v(st))
 
 
+@pytest.mark.parametrize("n_slots,n_heads,n_q,workgroups", [
+    (3000, 6, 300, 0),      # units < workgroup slots: grid a multiple of the units
+    (3000, 6, 300, 37),     # ranges crossing unit boundaries
+    (3000, 6, 300, 2048),   # more workgroups than fit on the chip at once
+    (300, 2, 100, 0),       # fewer (unit, tile) pairs than workgroups: empty ranges
+])
+def test_merge_schedule_leaves_results_unchanged(n_slots, n_heads, n_q, workgroups):
+    """Split units are merged by whichever workgroups take the blocks; with no
+    wait (merge_wait 0) the last arrival takes every block not already
+    committed.  Both schedules must give the same bits, and match the oracle."""
+    cfg = Config("merge", n_heads=n_heads, head_dim=128, n_slots=n_slots, chunk=0, seed=12,
+                 outliers=OutlierSpec(0.02, 8.0))
+    caches = [rkv.RingCache(1, n_slots, n_heads, 128, n_q, device=DEV, attn_workgroups=workgroups,
+                            attn_merge_wait_us=w) for w in (-1, 0)]
+    st = oring.RingState(n_slots, n_heads, 128)
+    s = Stream(cfg)
+    n = 2 * n_slots // 3
+    total = 2 * n  # the ring wraps
+    for p0 in (0, n):
+        _, k, v = s.chunk(n)
+        pos = positions(p0, n)
+        for c in caches:
+            c.write(0, to_dev(k), to_dev(v), pos_dev(pos))
+        oring.write(st, k.f64, v.f64, pos)
+    q, _, _ = s.chunk(n_q)
+    qpos = positions(total, n_q)
+    outs = []
+    for rep in range(2):  # a second call sees the arrival words the first left
+        for c in caches:
+            outs.append(c.attend(0, to_dev(q), pos_dev(qpos)))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    gate(f"merge schedule ({workgroups} workgroups)", gpu_out(outs[0]),
+         oatt.attend_exact(st, q.f64, qpos), oatt.sigma_v(st))
+
+
 def test_attend_rejects_bad_arguments():
     cache = rkv.RingCache(1, 64, 1, 64, 16, device=DEV)
     q = torch.zeros(17, 1, 64, dtype=torch.bfloat16, device=DEV)
