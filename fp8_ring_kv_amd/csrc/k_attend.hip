@@ -44,6 +44,8 @@
 // scale written to head h since the reset (kept by the write kernel).  The
 // running row maximum is raised only when a tile exceeds it by more than 2
 // (log2 units), so P <= 4 and P * s_v * c_h <= 448 always fits e4m3.
+#include <cmath>
+
 #include "rkv_launch.h"
 
 namespace rkv {
@@ -54,7 +56,7 @@ typedef __attribute__((address_space(1))) void global_void;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;  // LDS byte, addressed without a generic pointer
 
-constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLog2e = 1.4426950408889634;  // log2(e)
 constexpr float kLazy = 2.f;  // log2 headroom of the running maximum
 constexpr int kQG = 128;      // queries per unit: 4 waves x 32
 
@@ -67,7 +69,6 @@ struct AttnArgs {
   const uint4* q;
   const int32_t* q_pos;
   uint16_t* out;
-  float kscale;  // log2(e) / sqrt(D)
 };
 
 // Smallest e with amax <= 448 * 2^e (amax > 0): amax = f * 2^ex, f in [0.5, 1),
@@ -220,7 +221,6 @@ struct KOp {
 template <int D>
 struct VOp {
   v8i v[D / 32];
-  float sk[2];
 };
 
 __device__ inline v8i lds32(const lds_u8* p0, const lds_u8* p1) {
@@ -242,8 +242,8 @@ template <int D>
 struct TileOffsets {
   uint32_t k[D / 64][2];
   uint32_t v[2];
-  uint32_t s;    // key scale of slot 16 gq + lane % 16 (broadcast per register with DPP)
-  uint32_t sv4;  // value scales of slots 16 gq .. 16 gq + 15 (every lane of the half reads them)
+  uint32_t sk4;  // key scales of slots 16 gq .. 16 gq + 15 (every lane of the half reads them)
+  uint32_t sv4;  // value scales of the same slots
   __device__ TileOffsets(int lane) {
     const int li = lane & 31, gq = lane >> 5;
     const int krow = 16 * ((li >> 2) & 1) + 4 * (li >> 3) + (li & 3);
@@ -253,7 +253,7 @@ struct TileOffsets {
       for (int h = 0; h < 2; ++h) k[ks][h] = (uint32_t)(krow * D + 16 * ((4 * ks + 2 * gq + h) ^ ksw<D>(krow)));
 #pragma unroll
     for (int h = 0; h < 2; ++h) v[h] = (uint32_t)(TileLds<D>::V_OFF + 64 * li + 16 * ((gq + 2 * h) ^ vsw(li)));
-    s = (uint32_t)(TileLds<D>::S_OFF + 4 * (16 * gq + (lane & 15)));
+    sk4 = (uint32_t)(TileLds<D>::S_OFF + 64 * gq);
     sv4 = (uint32_t)(TileLds<D>::S_OFF + 256 + 64 * gq);
   }
 };
@@ -272,11 +272,6 @@ __device__ inline void read_v(VOp<D>& f, const lds_u8* lb, const TileOffsets<D>&
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)  // row block b: rows + 32 b, a constant offset (vsw ignores bit 5)
     f.v[b] = lds32(lb + 2048 * b + o.v[0], lb + 2048 * b + o.v[1]);
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    typedef __attribute__((address_space(3))) const float lds_f;
-    f.sk[sub] = *reinterpret_cast<lds_f*>(lb + o.s + 128 * sub);
-  }
 }
 
 template <int D, int TERMS>
@@ -299,26 +294,39 @@ struct WaveState {
 };
 
 // Softmax of one tile's S^T (in registers) and its P V product.
-// The probability scale c_h enters through the exponent: with l2c = log2 c_h,
-// P' = exp2(y - m + l2c) = P c_h, x = P' s_v, and the running sum l
-// accumulates P' (so the output is O / l).  The value scales of the 16
-// slots of a lane's half arrive as four 16-byte LDS reads that every lane of
-// the half shares, one value per accumulator register.
+// The queries carry the softmax scale log2(e)/sqrt(D), so S is in log2
+// units once multiplied by the key scale s_k.  Scores are kept relative to
+// mc = m - log2 c_h (m the running max): y - mc = fma(S, s_k, -mc), one
+// instruction per score, with the old mc; a tile that raises the max shifts
+// its scores by the change.  P' = exp2(y - mc) = P c_h, x = P' s_v, and the
+// running sum l accumulates P' (so the output is O / l).  The key and value
+// scales of the 16 slots of a lane's half arrive as 16-byte LDS reads that
+// every lane of the half shares, one value per accumulator register.
 template <int D, int TERMS>
 __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>& st,
-                                  unsigned long long mask, float kscale, float l2c, int lane,
-                                  const lds_u8* svp) {
+                                  unsigned long long mask, float l2c, int lane, const lds_u8* sp) {
   // x = P' s_v is formed once and reused; contracting x - e4m3(x) into
   // fma(P', s_v, -e4m3(x)) would recompute the product
 #pragma clang fp contract(off)
   constexpr int DB = D / 32;
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) const v4f lds_v4f;
   const int gq = lane >> 5;
-  const float tk0 = vf.sk[0] * kscale, tk1 = vf.sk[1] * kscale;
+  // before the first tile there is no max: scores relative to 0, and the
+  // first tile always raises the max
+  const float mcu = st.m == -INFINITY ? 0.f : st.m - l2c;
+  v4f sk[8];  // all eight reads issued before the first use
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    acc[0][r] *= bcast16(tk0, r);
-    acc[1][r] *= bcast16(tk1, r);
+  for (int w = 0; w < 8; ++w) sk[w] = *reinterpret_cast<lds_v4f*>(sp + 128 * (w >> 2) + 16 * (w & 3));
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int sub = w >> 2, r0 = 4 * (w & 3);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[sub][r0 + e] = __builtin_fmaf(acc[sub][r0 + e], sk[w][e], -mcu);
   }
+  v4f sv[8];  // value scales, read while the max is found
+#pragma unroll
+  for (int w = 0; w < 8; ++w) sv[w] = *reinterpret_cast<lds_v4f*>(sp + 256 + 128 * (w >> 2) + 16 * (w & 3));
   if (mask != ~0ull) {  // partially valid tile (ring edge, partial fill, padding)
     const uint32_t m0 = (uint32_t)(mask >> (16 * gq)) & 0xFFFFu;  // slots 16 gq + r
     const uint32_t m1 = (uint32_t)(mask >> (32 + 16 * gq)) & 0xFFFFu;
@@ -328,10 +336,10 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
       if (!((m1 >> r) & 1u)) acc[1][r] = -INFINITY;
     }
   }
-  float tmax = -INFINITY;
+  float tmax = fmaxf(acc[0][0], acc[1][0]);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(acc[0][r], acc[1][r]));
-  tmax = half_swap_max(tmax);
+  for (int r = 1; r < 16; ++r) tmax = fmaxf(fmaxf(tmax, acc[0][r]), acc[1][r]);  // max3 chain
+  tmax = half_swap_max(tmax) + mcu;  // the tile's max of y
   if (__ballot(tmax > st.m + kLazy) != 0ull) {
     const float mnew = fmaxf(st.m, tmax);
     const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
@@ -339,27 +347,29 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
 #pragma unroll
     for (int b = 0; b < DB; ++b) st.O[b] *= alpha;
     st.m = mnew;
+    const float shift = (mnew - l2c) - mcu;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc[0][r] -= shift;
+      acc[1][r] -= shift;
+    }
   }
-  // P <= 4 and s_v c_h <= 112, so the conversions below never overflow
-  // (fp32 rounding a hair above 448 still rounds to 448 in e4m3).
-  const float mc = st.m - l2c;
+  // P' <= 4 c_h and s_v c_h <= 112, so the conversions below never
+  // overflow (fp32 rounding a hair above 448 still rounds to 448 in e4m3).
   v8i ph, pl;
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     const int sub = w >> 2, r0 = 4 * (w & 3);
-    typedef float v4f __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) const v4f lds_v4f;
-    const v4f sv = *reinterpret_cast<lds_v4f*>(svp + 128 * sub + 4 * r0);
     float x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float p = __builtin_amdgcn_exp2f(acc[sub][r0 + e] - mc);
+      const float p = __builtin_amdgcn_exp2f(acc[sub][r0 + e]);
       st.l += p;
-      x[e] = p * sv[e];
+      x[e] = p * sv[w][e];
     }
     // (the low-half conversion keeps the high half of its third operand,
-    // which the high-half conversion overwrites: any register will do)
-    uint32_t hw = pack2_fp8<false>(x[0], x[1], __float_as_uint(x[0]));
+    // which the high-half conversion overwrites: any value will do)
+    uint32_t hw = pack2_fp8<false>(x[0], x[1], __builtin_nondeterministic_value(0u));
     hw = pack2_fp8<true>(x[2], x[3], hw);
     ph[w] = (int)hw;
     if (TERMS == 2) {  // second term: 16 (x - e4m3(x)), descaled by 2^-4
@@ -400,6 +410,7 @@ struct QPrepArgs {
   int nq_rows;  // 128-query groups of this call x 128
   const uint4* q;  // bf16 [n_q][H][D]
   const int32_t* q_pos;
+  float qscale;  // softmax scale in log2 units, log2(e) / sqrt(D), rounded once to float
 };
 
 template <int D, int TERMS>
@@ -434,8 +445,8 @@ __global__ __launch_bounds__(256) void q_prep_kernel(QPrepArgs A) {
       float cs, sn;
       rope_cs(p, turns[4 * c + m], cs, sn);
       const float x0 = active ? xv[2 * m] : 0.f, x1 = active ? xv[2 * m + 1] : 0.f;
-      y[8 * c + 2 * m] = x0 * cs - x1 * sn;
-      y[8 * c + 2 * m + 1] = x0 * sn + x1 * cs;
+      y[8 * c + 2 * m] = (x0 * cs - x1 * sn) * A.qscale;
+      y[8 * c + 2 * m + 1] = (x0 * sn + x1 * cs) * A.qscale;
       am = fmaxf(am, fmaxf(fabsf(y[8 * c + 2 * m]), fabsf(y[8 * c + 2 * m + 1])));
     }
   }
@@ -767,7 +778,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
       int rel = sl - a;
       if (rel < 0) rel += N;
       const unsigned long long mask = __ballot(sl < N && rel < nv);
-      softmax_pv<D, TERMS>(sacc, vf, st, mask, A.kscale, l2c, lane, lb + off.sv4);
+      softmax_pv<D, TERMS>(sacc, vf, st, mask, l2c, lane, lb + off.sk4);
     }
 
     __builtin_amdgcn_s_setprio(0);
@@ -879,6 +890,7 @@ hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void*
   P.nq_rows = nqg * kQG;
   P.q = (const uint4*)q;
   P.q_pos = q_pos;
+  P.qscale = (float)(kLog2e / std::sqrt((double)D));
   const int rows = g.n_heads * P.nq_rows, rows_per_block = 256 / 8;
   const dim3 pgrid((rows + rows_per_block - 1) / rows_per_block);
   if (D == 128) {
@@ -900,7 +912,6 @@ hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void*
   A.q = (const uint4*)q;
   A.q_pos = q_pos;
   A.out = (uint16_t*)out;
-  A.kscale = kLog2e / sqrtf((float)D);
   // With at most one workgroup slot per unit, the grid is a multiple of the
   // unit count (preferably also of the 8 XCDs), so that every workgroup's
   // range lies inside one unit: one segment per workgroup, equal splits.

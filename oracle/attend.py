@@ -20,13 +20,19 @@ Three precisions, all on the dequantized cache:
 The device kernel's declared numerics, which ``attend_method`` and
 ``attend_emul`` follow:
 
-* Q quantization: per (token, head), a power-of-two scale 2**e with e the
-  smallest integer such that amax(q) <= 448 * 2**e; codes = e4m3(q / 2**e).
+* Softmax scale: the kernel multiplies each RoPE'd query by
+  c_s = log2(e) / sqrt(D), rounded once to float32, before quantizing it, so
+  the logits come out in log2 units and P = 2**(S - m).  (The pages fix FP8
+  attention but not where the scale enters; applied to Q it costs no work
+  per logit.)
+* Q quantization: of the scaled query, per (token, head), a power-of-two
+  scale 2**e with e the smallest integer such that amax(q) <= 448 * 2**e;
+  codes = e4m3(q / 2**e).
   (A power of two is applied exactly inside the FP8 matrix instruction.)
   With two terms (the default, "precise" mode) the residual
   r = q - decode(codes) * 2**e is quantized the same way and the kernel
   multiplies K by both terms; Q is then known to about 2**-8 relative.
-* P.V in FP8: with P = exp(S - m) (m the row maximum), the kernel feeds
+* P.V in FP8: with P = 2**(S - m) (m the row maximum), the kernel feeds
   x = P * s_v[j] * c with c = 448 * 2**-headroom / vmax_h, vmax_h the largest
   value scale written to the head since the last reset (an upper bound of
   every cached s_v), as hi = e4m3(x) and, with two terms, as
@@ -74,6 +80,18 @@ def _prepare(st: RingState, q: np.ndarray, q_pos: np.ndarray):
     slots = valid_slots(st)
     qr = rope(q, q_pos, st.rope_base)  # [n_q, H, D]
     return qr, slots
+
+
+def softmax_scale_log2(d: int) -> float:
+    """The kernel's query factor c_s = log2(e) / sqrt(D), rounded once to float32."""
+    return float(np.float32(math.log2(math.e) / math.sqrt(d)))
+
+
+def _softmax2_av(sh: np.ndarray, vh: np.ndarray) -> np.ndarray:
+    """softmax in base 2 of logits already in log2 units, times v; float64."""
+    sh = sh - sh.max(axis=1, keepdims=True)
+    p = np.exp2(sh)
+    return (p @ vh) / p.sum(axis=1, keepdims=True)
 
 
 def _softmax_av(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray) -> np.ndarray:
@@ -125,11 +143,11 @@ def attend_method(st: RingState, q: np.ndarray, q_pos: np.ndarray, q_terms: int 
     out = np.zeros(qr.shape, dtype=np.float64)
     if slots.size == 0:
         return out
-    qd = quantize_q_terms(qr, q_terms)
+    qd = quantize_q_terms(qr * softmax_scale_log2(st.head_dim), q_terms)
     kd = dequant_k(st)[:, slots, :]
     vd = dequant_v(st)[:, slots, :]
     for h in range(st.n_heads):
-        out[:, h, :] = _softmax_av(qd[:, h, :], kd[h], vd[h])
+        out[:, h, :] = _softmax2_av(qd[:, h, :] @ kd[h].T, vd[h])
     return out
 
 
@@ -140,14 +158,13 @@ def attend_emul(st: RingState, q: np.ndarray, q_pos: np.ndarray, q_terms: int = 
     out = np.zeros(qr.shape, dtype=np.float64)
     if slots.size == 0:
         return out
-    qd = quantize_q_terms(qr, q_terms)
+    qd = quantize_q_terms(qr * softmax_scale_log2(st.head_dim), q_terms)
     kd = dequant_k(st)[:, slots, :]
     v8 = e4m3.decode(st.codes_v[:, slots, :])  # codes as values
     sv = st.scale_v[:, slots]  # [H, n_valid]
-    d = st.head_dim
     for h in range(st.n_heads):
-        s = qd[:, h, :] @ kd[h].T / math.sqrt(d)
-        p = np.exp(s - s.max(axis=1, keepdims=True))  # <= 1, row max exactly 1
+        s = qd[:, h, :] @ kd[h].T  # log2 units
+        p = np.exp2(s - s.max(axis=1, keepdims=True))  # <= 1, row max exactly 1
         l = p.sum(axis=1, keepdims=True)
         smax = st.vmax[h]
         c = (e4m3.E4M3_MAX * 2.0 ** (-headroom) / smax) if smax > 0 else 1.0

@@ -150,16 +150,30 @@ def test_reset_is_a_global_position_shift():
 
 
 def test_lossless_queries_make_method_equal_exact():
-    """Queries whose RoPE'd values are e4m3 values times 2**e quantize without loss."""
+    """Queries whose scaled RoPE'd values are e4m3 values times 2**e quantize
+    without loss: the method is then exact attention, with the float32
+    softmax factor in place of log2(e)/sqrt(D)."""
     rng = np.random.default_rng(6)
     st = ring.RingState(48, 2, 16)
     ring.write(st, rng.standard_normal((48, 2, 16)), rng.standard_normal((48, 2, 16)), np.arange(48))
     grid = e4m3.decode(np.arange(0, 0x7F, dtype=np.uint8))
-    qr = rng.choice(grid, size=(6, 2, 16)) * rng.choice([-1.0, 1.0], size=(6, 2, 16)) * 2.0 ** -5
+    cs = attend.softmax_scale_log2(16)
+    assert abs(cs - math.log2(math.e) / 4.0) <= 2.0 ** -24 * cs  # one float32 rounding
+    qg = rng.choice(grid, size=(6, 2, 16)) * rng.choice([-1.0, 1.0], size=(6, 2, 16)) * 2.0 ** -5
+    qr = qg / cs  # qr * cs rounds back to qg: well inside half an e4m3 step
     q_pos = np.zeros(6, dtype=np.int64)  # position 0: RoPE is the identity
-    a = attend.attend_exact(st, qr, q_pos)
     b = attend.attend_method(st, qr, q_pos)
-    assert np.max(np.abs(a - b)) < 1e-14
+    # exact attention of the grid queries in base 2, by explicit loops
+    kd, vd = ring.dequant_k(st), ring.dequant_v(st)
+    want = np.zeros_like(b)
+    for t in range(6):
+        for h in range(2):
+            s = [sum(qg[t, h, i] * kd[h, j, i] for i in range(16)) for j in range(48)]
+            w = [2.0 ** (x - max(s)) for x in s]
+            want[t, h] = sum(w[j] * vd[h, j] for j in range(48)) / sum(w)
+    assert np.max(np.abs(b - want)) < 1e-13
+    # and the factor's rounding moves exact natural-base attention by ~1e-7 at most
+    assert np.max(np.abs(attend.attend_exact(st, qr, q_pos) - b)) < 1e-5
 
 
 def test_quantize_q_pow2_closed_forms():
