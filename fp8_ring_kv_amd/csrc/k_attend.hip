@@ -480,7 +480,7 @@ __global__ __launch_bounds__(256) void q_prep_kernel(QPrepArgs A) {
     } else {
       *reinterpret_cast<uint2*>(dst) = make_uint2(wd[0], wd[1]);
     }
-    if (part == 0) A.ws.qexp[row] = e;
+    if (part == 0) A.ws.qexp[row] = 127 + e;  // E8M0 code of 2^e
     am = nm;
   }
 }
@@ -678,6 +678,26 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
   const int li = lane & 31, gq = lane >> 5;
 
   const LayerPtrs L = layer_ptrs(g, A.layer);
+  const int U = A.nqg * H;
+  // This wave's 32 prepared queries of unit u (B operand of S^T = K Q^T).
+  v8i qf[TERMS][KS];
+  int qs[TERMS];
+  auto load_q = [&](int u) {
+    const int h = u / A.nqg, qi = kQG * (u % A.nqg) + 32 * wave + li;
+#pragma unroll
+    for (int t = 0; t < TERMS; ++t) {
+      const size_t row = ((size_t)t * H + h) * A.ws.nq_pad + qi;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[t][ks] = gload32(A.ws.qcodes + row * D + 64 * ks + 32 * gq);
+      qs[t] = A.ws.qexp[row];
+    }
+  };
+  // With a grid that is a multiple of the unit count, every range lies in
+  // unit gi / (G / U) whatever the ring holds: its queries load while the
+  // ring state is read.
+  const int u_pre = G % U == 0 ? gi / (G / U) : -1;
+  if (u_pre >= 0) load_q(u_pre);
+
   const int head = L.state[0], nv = L.state[1];
   int a = head - nv;
   if (a < 0) a += N;
@@ -688,7 +708,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
     count = e < N ? e / kTile - T0 + 1 : (NT - T0) + (e - N) / kTile + 1;
     if (count > NT) count = NT;
   }
-  const int U = A.nqg * H;
 
   if (count == 0) {  // empty cache: every output row is zero
     for (int u = gi; u < U; u += G) {
@@ -734,18 +753,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
     src.svb = L.scale_v + (size_t)h * NP;
     auto buf = [&](int tj) { return kv0 + (tj % kBufs) * KVB; };
 
-    // ---- 1. this wave's 32 prepared queries (B operand of S^T = K Q^T),
-    //         then the copies of the first pair of tiles ----
+    // ---- 1. the unit's queries (unless already loaded), then the copies of
+    //         the first pair of tiles ----
     const int qi = kQG * qg + 32 * wave + li;
-    v8i qf[TERMS][KS];
-    int qs[TERMS];
-#pragma unroll
-    for (int t = 0; t < TERMS; ++t) {
-      const size_t row = ((size_t)t * H + h) * A.ws.nq_pad + qi;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[t][ks] = gload32(A.ws.qcodes + row * D + 64 * ks + 32 * gq);
-      qs[t] = 127 + A.ws.qexp[row];
-    }
+    if (u != u_pre) load_q(u);
     for (int tj = 0; tj < 2 && tj < nk; ++tj) copy_tile<D>(buf(tj), src, tile_of(t_lo + tj), coff, wave, lane);
 
     // ---- 2. the segment's tiles, in pairs.  Tile t sits in buffer t % 4.

@@ -20,7 +20,7 @@ struct AttnWs {
   // (high half); zeroed for the call's units by q_prep_kernel
   unsigned long long* sync;
   uint8_t* qcodes; // [2 terms][H][nq_pad][D] e4m3 codes of the RoPE'd queries
-  int32_t* qexp;   // [2 terms][H][nq_pad] power-of-two exponent of each query row and term
+  int32_t* qexp;   // [2 terms][H][nq_pad] E8M0 code (127 + e) of the 2^e scale of each query row and term
   int32_t nq_pad;  // max_queries rounded up to 128
   int32_t grid;    // persistent workgroups
   int32_t terms;   // 2 = precise, 1 = fast
