@@ -4,7 +4,8 @@ One step is the per-call cache work of a block forward in the pages'
 workload (Runway Characters paper, §2 "The step budget", §4, Appendix G):
 write the 757 new tokens of the chunk into the 5,788-slot ring (RoPE + FP8
 quantization fused), then attend the chunk's 757 queries over every slot,
-12 heads x 128 (one GPU's head share).  Every 42nd step is preceded by the
+12 heads x 128 (one GPU's head share) -- one cache_write_attend call, which
+prepares the queries in the write's launch.  Every 42nd step is preceded by the
 position reset: a delta rotation of every cached key by -42 * 757.  The
 cache starts full with its ring head at slot 3,100 (8,888 tokens written).
 
@@ -167,8 +168,7 @@ def graph_step_ms(args, cache, pool, pos_pool, out, stream):
                 if j == 0:
                     cache.rotate(0, -RESET_EVERY * CHUNK)
                 q, k, v = pool[j]
-                cache.write(0, k, v, pos_pool[j])
-                cache.attend(0, q, pos_pool[j], out)
+                cache.write_attend(0, k, v, pos_pool[j], q, pos_pool[j], out)
             graphs.append(g)
     stream.wait_stream(side)
     torch.cuda.synchronize()
@@ -232,8 +232,7 @@ def main():
         if j == 0 and i > 0:
             cache.rotate(0, -RESET_EVERY * CHUNK)
         q, k, v = pool[j]
-        cache.write(0, k, v, pos_pool[j])
-        cache.attend(0, q, pos_pool[j], out)
+        cache.write_attend(0, k, v, pos_pool[j], q, pos_pool[j], out)
 
     for i in range(args.warmup):
         step_fast(i)

@@ -23,6 +23,7 @@ __all__ = [
     "rkv_params", "rkv_layout", "RkvError", "lib", "lib_path",
     "ring_cache_bytes", "ring_cache_create", "ring_cache_destroy", "ring_cache_reset",
     "ring_cache_layout", "cache_write_rope_fp8", "cache_delta_rotate", "cache_attend",
+    "cache_write_attend",
     "rkv_last_error", "RingCache",
 ]
 
@@ -100,6 +101,8 @@ def lib() -> ctypes.CDLL:
     L.cache_delta_rotate.restype = ctypes.c_int
     L.cache_attend.argtypes = [VP, I32, VP, VP, I32, VP, VP]
     L.cache_attend.restype = ctypes.c_int
+    L.cache_write_attend.argtypes = [VP, I32, VP, VP, VP, I32, VP, VP, I32, VP, VP]
+    L.cache_write_attend.restype = ctypes.c_int
     L.rkv_last_error.argtypes = []
     L.rkv_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -161,6 +164,15 @@ def cache_attend(handle: int, layer: int, q: int, q_pos: int, n_q: int, out: int
                             n_q, ctypes.c_void_p(out), ctypes.c_void_p(stream))
     if rc != RKV_OK:
         raise RkvError(rc, "cache_attend")
+
+
+def cache_write_attend(handle: int, layer: int, k: int, v: int, pos: int, n: int, q: int, q_pos: int,
+                       n_q: int, out: int, stream: int) -> None:
+    rc = lib().cache_write_attend(ctypes.c_void_p(handle), layer, ctypes.c_void_p(k), ctypes.c_void_p(v),
+                                  ctypes.c_void_p(pos), n, ctypes.c_void_p(q), ctypes.c_void_p(q_pos), n_q,
+                                  ctypes.c_void_p(out), ctypes.c_void_p(stream))
+    if rc != RKV_OK:
+        raise RkvError(rc, "cache_write_attend")
 
 
 # ---- torch-facing wrapper ---------------------------------------------------
@@ -234,6 +246,23 @@ class RingCache:
         _check(out, torch.bfloat16, shape, "out")
         cache_attend(self.handle, layer, q.data_ptr(), q_pos.data_ptr(), n_q, out.data_ptr(),
                      _stream_handle(stream))
+        return out
+
+    def write_attend(self, layer: int, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor, q: torch.Tensor,
+                     q_pos: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """write(layer, k, v, pos) then attend(layer, q, q_pos, out) in one call."""
+        n, n_q = k.shape[0], q.shape[0]
+        _check(k, torch.bfloat16, (n, self.n_heads, self.head_dim), "k")
+        _check(v, torch.bfloat16, (n, self.n_heads, self.head_dim), "v")
+        _check(pos, torch.int32, (n,), "pos")
+        shape = (n_q, self.n_heads, self.head_dim)
+        _check(q, torch.bfloat16, shape, "q")
+        _check(q_pos, torch.int32, (n_q,), "q_pos")
+        if out is None:
+            out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
+        _check(out, torch.bfloat16, shape, "out")
+        cache_write_attend(self.handle, layer, k.data_ptr(), v.data_ptr(), pos.data_ptr(), n, q.data_ptr(),
+                           q_pos.data_ptr(), n_q, out.data_ptr(), _stream_handle(stream))
         return out
 
     def reset(self, layer: int = -1, stream=None):

@@ -47,6 +47,7 @@
 #include <cmath>
 
 #include "rkv_launch.h"
+#include "write_body.h"
 
 namespace rkv {
 
@@ -413,15 +414,16 @@ struct QPrepArgs {
   float qscale;  // softmax scale in log2 units, log2(e) / sqrt(D), rounded once to float
 };
 
+// Body of one 256-thread workgroup number `block` of the preparation.
 template <int D, int TERMS>
-__global__ __launch_bounds__(256) void q_prep_kernel(QPrepArgs A) {
+__device__ inline void q_prep_body(const QPrepArgs& A, int block) {
   constexpr int TPR = 8;          // threads per row
   constexpr int EPT = D / TPR;    // elements per thread: 16 or 8
   const int H = A.g.n_heads;
-  const int r = (int)((blockIdx.x * 256 + threadIdx.x) / TPR);  // h * nq_rows + qi
+  const int r = (int)((block * 256 + threadIdx.x) / TPR);  // h * nq_rows + qi
   const int part = (int)(threadIdx.x % TPR);
   {  // the arrival words of this call's units start at zero
-    const int gt = (int)(blockIdx.x * 256 + threadIdx.x);
+    const int gt = (int)(block * 256 + threadIdx.x);
     if (gt < H * (A.nq_rows / 128)) A.ws.sync[(size_t)gt * kSyncStride] = 0ull;
   }
   if (r >= H * A.nq_rows) return;  // whole rows only: the reductions stay inside live lanes
@@ -483,6 +485,33 @@ __global__ __launch_bounds__(256) void q_prep_kernel(QPrepArgs A) {
     if (part == 0) A.ws.qexp[row] = 127 + e;  // E8M0 code of 2^e
     am = nm;
   }
+}
+
+template <int D, int TERMS>
+__global__ __launch_bounds__(256) void q_prep_kernel(QPrepArgs A) {
+  q_prep_body<D, TERMS>(A, (int)blockIdx.x);
+}
+
+// Write and query preparation in one launch (D = 128: both use 256-thread
+// workgroups): the first wgx * wgy workgroups write the new tokens, the rest
+// prepare the queries.  The two touch disjoint memory.
+struct WritePrepArgs {
+  QPrepArgs P;
+  int layer;
+  const uint4* k;
+  const uint4* v;
+  const int32_t* pos;
+  int n;
+  int wgx, wgy;  // the write's grid
+};
+
+template <int HG, int TERMS>
+__global__ __launch_bounds__(256) void write_prep_kernel(WritePrepArgs W) {
+  const int b = (int)blockIdx.x, nw = W.wgx * W.wgy;
+  if (b < nw)
+    write_rope_fp8_body<128, HG>(W.P.g, W.layer, W.k, W.v, W.pos, W.n, b % W.wgx, b / W.wgx, W.wgx, W.wgy);
+  else
+    q_prep_body<128, TERMS>(W.P, b - nw);
 }
 
 __device__ inline v8i gload32(const uint8_t* p) {
@@ -890,30 +919,29 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
   }
 }
 
-hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void* q,
-                         const int32_t* q_pos, int n_q, void* out, hipStream_t s) {
-  const int D = g.head_dim;
-  const int nqg = (n_q + kQG - 1) / kQG;
+static QPrepArgs make_prep_args(const Geom& g, const AttnWs& ws, const void* q, const int32_t* q_pos, int n_q) {
   QPrepArgs P;
   P.g = g;
   P.ws = ws;
   P.n_q = n_q;
-  P.nq_rows = nqg * kQG;
+  P.nq_rows = ((n_q + kQG - 1) / kQG) * kQG;
   P.q = (const uint4*)q;
   P.q_pos = q_pos;
-  P.qscale = (float)(kLog2e / std::sqrt((double)D));
-  const int rows = g.n_heads * P.nq_rows, rows_per_block = 256 / 8;
-  const dim3 pgrid((rows + rows_per_block - 1) / rows_per_block);
-  if (D == 128) {
-    if (ws.terms == 2) hipLaunchKernelGGL((q_prep_kernel<128, 2>), pgrid, dim3(256), 0, s, P);
-    else hipLaunchKernelGGL((q_prep_kernel<128, 1>), pgrid, dim3(256), 0, s, P);
-  } else {
-    if (ws.terms == 2) hipLaunchKernelGGL((q_prep_kernel<64, 2>), pgrid, dim3(256), 0, s, P);
-    else hipLaunchKernelGGL((q_prep_kernel<64, 1>), pgrid, dim3(256), 0, s, P);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  P.qscale = (float)(kLog2e / std::sqrt((double)g.head_dim));
+  return P;
+}
 
+static int prep_blocks(const QPrepArgs& P) {
+  const int rows = P.g.n_heads * P.nq_rows, rows_per_block = 256 / 8;
+  return (rows + rows_per_block - 1) / rows_per_block;
+}
+
+// The attention kernel alone (its queries prepared by an earlier launch on
+// the stream).
+static hipError_t launch_attend_main(const Geom& g, const AttnWs& ws, int layer, const void* q,
+                                     const int32_t* q_pos, int n_q, void* out, hipStream_t s) {
+  const int D = g.head_dim;
+  const int nqg = (n_q + kQG - 1) / kQG;
   AttnArgs A;
   A.g = g;
   A.ws = ws;
@@ -943,6 +971,55 @@ hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void*
     else hipLaunchKernelGGL((attend_kernel<64, 1>), grid, dim3(64 * kWaves), 0, s, A);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void* q,
+                         const int32_t* q_pos, int n_q, void* out, hipStream_t s) {
+  const QPrepArgs P = make_prep_args(g, ws, q, q_pos, n_q);
+  const dim3 pgrid(prep_blocks(P));
+  if (g.head_dim == 128) {
+    if (ws.terms == 2) hipLaunchKernelGGL((q_prep_kernel<128, 2>), pgrid, dim3(256), 0, s, P);
+    else hipLaunchKernelGGL((q_prep_kernel<128, 1>), pgrid, dim3(256), 0, s, P);
+  } else {
+    if (ws.terms == 2) hipLaunchKernelGGL((q_prep_kernel<64, 2>), pgrid, dim3(256), 0, s, P);
+    else hipLaunchKernelGGL((q_prep_kernel<64, 1>), pgrid, dim3(256), 0, s, P);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attend_main(g, ws, layer, q, q_pos, n_q, out, s);
+}
+
+template <int HG>
+static void launch_write_prep_t(const WritePrepArgs& W, int blocks, int terms, hipStream_t s) {
+  if (terms == 2) hipLaunchKernelGGL((write_prep_kernel<HG, 2>), dim3(blocks), dim3(256), 0, s, W);
+  else hipLaunchKernelGGL((write_prep_kernel<HG, 1>), dim3(blocks), dim3(256), 0, s, W);
+}
+
+hipError_t launch_write_attend(const Geom& g, const AttnWs& ws, int layer, const void* k, const void* v,
+                               const int32_t* pos, int n, const void* q, const int32_t* q_pos, int n_q,
+                               void* out, hipStream_t s) {
+  if (g.head_dim != 128) {  // 128-thread write workgroups: two launches, then the attention
+    hipError_t e = launch_write(g, layer, k, v, pos, n, s);
+    if (e != hipSuccess) return e;
+    return launch_attend(g, ws, layer, q, q_pos, n_q, out, s);
+  }
+  WritePrepArgs W;
+  W.P = make_prep_args(g, ws, q, q_pos, n_q);
+  W.layer = layer;
+  W.k = (const uint4*)k;
+  W.v = (const uint4*)v;
+  W.pos = pos;
+  W.n = n;
+  int hg;
+  write_grid(g, n, &W.wgx, &hg);
+  W.wgy = g.n_heads / hg;
+  const int blocks = W.wgx * W.wgy + prep_blocks(W.P);
+  if (hg == 4) launch_write_prep_t<4>(W, blocks, ws.terms, s);
+  else if (hg == 2) launch_write_prep_t<2>(W, blocks, ws.terms, s);
+  else launch_write_prep_t<1>(W, blocks, ws.terms, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attend_main(g, ws, layer, q, q_pos, n_q, out, s);
 }
 
 }  // namespace rkv

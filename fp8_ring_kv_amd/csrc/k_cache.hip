@@ -13,6 +13,7 @@
 // is a reduction across the lanes of that row (no LDS round trip except for
 // the V transpose).
 #include "rkv_launch.h"
+#include "write_body.h"
 
 namespace rkv {
 
@@ -67,184 +68,13 @@ hipError_t launch_reset(const Geom& g, int layer_lo, int layer_hi, hipStream_t s
 }
 
 // ---------------------------------------------------------------------------
-// Fused write.  One workgroup per (16-slot group of the ring, HG heads).  The
-// groups touched by a write of n tokens are consecutive (mod the group count
-// ceil(N/16), pad slots excluded) starting at the group holding `head`; a
-// contiguous run of n slots meets at most n/16 + 2 of them (one partial group
-// at each end, plus the short last group when it wraps).  The grid covers
-// that many and each thread works out from the device-side head whether its
-// slot is written and by which token: token i = (slot - head) mod N, written
-// iff i < n.  Thread (tau, lane) owns 8 elements of token row tau in each of
-// the HG heads: its loads for all heads are in flight together and its RoPE
-// cos/sin serve all of them.
+// Fused write (the body is in write_body.h).
 template <int D, int HG>
 __global__ __launch_bounds__(16 * (D / 8)) void write_rope_fp8_kernel(
     Geom g, int layer, const uint4* __restrict__ k, const uint4* __restrict__ v,
     const int32_t* __restrict__ pos, int n) {
-  constexpr int LPR = D / 8;  // lanes per token row
-  __shared__ uint2 vcodes[HG][16][LPR];
-  __shared__ float vmx[HG][16];
-
-  const LayerPtrs L = layer_ptrs(g, layer);
-  const int N = g.n_slots, NP = g.n_pad, H = g.n_heads;
-  const int head = L.state[0];
-  const int nvalid = L.state[1];
-  const int h0 = blockIdx.y * HG;
-  const int NG = (N + 15) / 16;  // 16-slot groups of the ring (the last may be short)
-  const int G = (head / 16 + (int)blockIdx.x) % NG;
-  const int tau = threadIdx.x / LPR;
-  const int lane = threadIdx.x % LPR;
-  const int slot = 16 * G + tau;
-  int i = slot - head;
-  if (i < 0) i += N;
-  const bool active = slot < N && i < n;
-
-  uint4 kw[HG], vw[HG];
-  int32_t p = 0;
-#pragma unroll
-  for (int hh = 0; hh < HG; ++hh) kw[hh] = vw[hh] = make_uint4(0u, 0u, 0u, 0u);
-  if (active) {
-    const size_t row = ((size_t)i * H + h0) * LPR + lane;
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      kw[hh] = k[row + hh * LPR];
-      vw[hh] = v[row + hh * LPR];
-    }
-    p = pos[i];
-  }
-  // Tickets for the device-side write position, taken once head and n_valid
-  // are read (and after the row loads are issued: a returning atomic holds
-  // up every later load's wait): whoever takes the last ticket knows every
-  // workgroup has read them and may advance them.  Workgroup w takes a ticket on
-  // sub-counter w % kSub; the last arrival of each sub-group takes one on the
-  // top counter, so no counter sees more than ceil(total / kSub) atomics.
-  // The increment depends on the loaded head (it is always 1), so it cannot
-  // be issued before the load returns.  No workgroup reads what another one
-  // writes, so relaxed device-scope atomics suffice; the next kernel on the
-  // stream sees the new state.
-  // (The returned ticket is looked at only at the end of the kernel.)
-  const int wg = (int)(blockIdx.y * gridDim.x + blockIdx.x);
-  int t1 = 0;
-  if (threadIdx.x == 0)
-    t1 = __hip_atomic_fetch_add(&L.state[4 + wg % kSub], head < 0x7FFFFFFF ? 1 : 2, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-  // angles for every lane (the table index is always in range; inactive
-  // lanes rotate zeros), so the four table loads issue together
-  float cs[4], sn[4];
-  const double* turns = omega_turns(g);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) rope_cs(p, turns[4 * lane + m], cs[m], sn[m]);
-
-#pragma unroll
-  for (int hh = 0; hh < HG; ++hh) {
-    const float x[8] = {bf16_lo(kw[hh].x), bf16_hi(kw[hh].x), bf16_lo(kw[hh].y), bf16_hi(kw[hh].y),
-                        bf16_lo(kw[hh].z), bf16_hi(kw[hh].z), bf16_lo(kw[hh].w), bf16_hi(kw[hh].w)};
-    const float u[8] = {bf16_lo(vw[hh].x), bf16_hi(vw[hh].x), bf16_lo(vw[hh].y), bf16_hi(vw[hh].y),
-                        bf16_lo(vw[hh].z), bf16_hi(vw[hh].z), bf16_lo(vw[hh].w), bf16_hi(vw[hh].w)};
-    float y[8];
-    float ak = 0.f, av = 0.f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      y[2 * m] = x[2 * m] * cs[m] - x[2 * m + 1] * sn[m];
-      y[2 * m + 1] = x[2 * m] * sn[m] + x[2 * m + 1] * cs[m];
-      ak = fmaxf(ak, fmaxf(fabsf(y[2 * m]), fabsf(y[2 * m + 1])));
-      av = fmaxf(av, fmaxf(fabsf(u[2 * m]), fabsf(u[2 * m + 1])));
-    }
-    ak = group_max<LPR>(ak);
-    av = group_max<LPR>(av);
-    // scale s = fp32(margin * amax / 448); codes = e4m3(y / s)
-    const float sk = ak * g.margin / kE4M3Max, sv = av * g.margin / kE4M3Max;
-    const float rk = sk > 0.f ? 1.f / sk : 0.f;
-    const float rv = sv > 0.f ? 1.f / sv : 0.f;
-    // keys are fp32 RoPE results (a rounding away from the exact rotation
-    // already), values are raw bf16 whose quotients often sit on e4m3 midpoints
-    uint2 ck, cv;
-    ck.x = pack2_fp8<false>(quant_mul(y[0], rk), quant_mul(y[1], rk), 0u);
-    ck.x = pack2_fp8<true>(quant_mul(y[2], rk), quant_mul(y[3], rk), ck.x);
-    ck.y = pack2_fp8<false>(quant_mul(y[4], rk), quant_mul(y[5], rk), 0u);
-    ck.y = pack2_fp8<true>(quant_mul(y[6], rk), quant_mul(y[7], rk), ck.y);
-    cv.x = pack2_fp8<false>(quant_div(u[0], sv, rv), quant_div(u[1], sv, rv), 0u);
-    cv.x = pack2_fp8<true>(quant_div(u[2], sv, rv), quant_div(u[3], sv, rv), cv.x);
-    cv.y = pack2_fp8<false>(quant_div(u[4], sv, rv), quant_div(u[5], sv, rv), 0u);
-    cv.y = pack2_fp8<true>(quant_div(u[6], sv, rv), quant_div(u[7], sv, rv), cv.y);
-    if (active) {
-      const size_t r = (size_t)(h0 + hh) * NP + slot;
-      *reinterpret_cast<uint2*>(L.codes_k + r * D + 8 * lane) = ck;
-      if (lane == 0) {
-        L.scale_k[r] = sk;
-        L.scale_v[r] = sv;
-      }
-    }
-    vcodes[hh][tau][lane] = cv;
-    if (lane == 0) vmx[hh][tau] = active ? sv : 0.f;
-  }
-  if (active && lane == 0 && h0 == 0) L.slot_pos[slot] = p;
-  // LDS-only barrier: the transpose below needs the LDS writes above, not
-  // the global stores (a __syncthreads fence would wait for those too)
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  // V: transposed 64-slot tiles, row d holds the tile's slots in order.  The
-  // group's 16 slots are 16 consecutive bytes of each row; thread t writes
-  // 8 of them (tokens 8*half .. 8*half+7) of row d, for each head.
-  {
-    const int t = threadIdx.x;
-    const int d = t >> 1, half = t & 1;
-    bool act[8];
-    int nact = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sl = 16 * G + 8 * half + e;
-      int ii = sl - head;
-      if (ii < 0) ii += N;
-      act[e] = sl < N && ii < n;
-      nact += act[e];
-    }
-    const int T = (16 * G) / kTile, w0 = (16 * G) % kTile;
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      const uint8_t* vb = reinterpret_cast<const uint8_t*>(vcodes[hh]);
-      uint32_t b[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) b[e] = vb[(8 * half + e) * D + d];
-      uint8_t* dst = L.codes_v + (((size_t)(h0 + hh) * g.n_tiles + T) * D + d) * kTile + w0 + 8 * half;
-      if (nact == 8) {
-        uint2 w;
-        w.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-        w.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-        *reinterpret_cast<uint2*>(dst) = w;
-      } else if (nact > 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (act[e]) dst[e] = (uint8_t)b[e];
-      }
-    }
-  }
-
-  // Running per-head maximum of the value scales (non-negative floats order
-  // like their bit patterns); nothing waits for these atomics.
-  if ((int)threadIdx.x < HG) {
-    float mx = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, vmx[threadIdx.x][e]);
-    if (mx > 0.f) atomicMax(&L.vmax[(h0 + threadIdx.x) * kSub + blockIdx.x % kSub], __float_as_uint(mx));
-  }
-  // The last arrival of each sub-group takes a ticket on the top counter;
-  // the last of those advances the write position.
-  if (threadIdx.x == 0) {
-    const int total = (int)(gridDim.x * gridDim.y);
-    const int k = wg % kSub;
-    const int ksize = (total - k + kSub - 1) / kSub;  // workgroups with wg % kSub == k
-    const int nsub = total < kSub ? total : kSub;
-    if (t1 == ksize - 1) {
-      __hip_atomic_store(&L.state[4 + k], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int t2 = __hip_atomic_fetch_add(&L.state[2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (t2 == nsub - 1) {
-        __hip_atomic_store(&L.state[2], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        L.state[0] = (int)(((long long)head + n) % N);
-        L.state[1] = nvalid + n < N ? nvalid + n : N;
-      }
-    }
-  }
+  write_rope_fp8_body<D, HG>(g, layer, k, v, pos, n, (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x,
+                             (int)gridDim.y);
 }
 
 template <int D, int HG>
@@ -257,11 +87,8 @@ static void launch_write_t(const Geom& g, int layer, const void* k, const void* 
 
 hipError_t launch_write(const Geom& g, int layer, const void* k, const void* v, const int32_t* pos,
                         int n, hipStream_t s) {
-  const int NG = (g.n_slots + 15) / 16;
-  int groups = (n + 15) / 16 + 2;
-  if (groups > NG) groups = NG;
-  const int H = g.n_heads;
-  const int hg = H % 4 == 0 ? 4 : (H % 2 == 0 ? 2 : 1);
+  int groups, hg;
+  write_grid(g, n, &groups, &hg);
   if (g.head_dim == 128) {
     if (hg == 4) launch_write_t<128, 4>(g, layer, k, v, pos, n, groups, s);
     else if (hg == 2) launch_write_t<128, 2>(g, layer, k, v, pos, n, groups, s);

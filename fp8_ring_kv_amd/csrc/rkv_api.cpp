@@ -291,4 +291,25 @@ int cache_attend(rkv_cache* c, int32_t layer, const void* q_bf16, const int32_t*
   return RKV_OK;
 }
 
+int cache_write_attend(rkv_cache* c, int32_t layer, const void* k_bf16, const void* v_bf16,
+                       const int32_t* pos, int32_t n, const void* q_bf16, const int32_t* q_pos,
+                       int32_t n_q, void* out_bf16, hipStream_t stream) {
+  if (!c) return fail(RKV_EINVAL, "cache is null");
+  int lo, hi;
+  if (int r = layer_range(c, layer, false, &lo, &hi)) return r;
+  if (!k_bf16 || !v_bf16 || !pos || !q_bf16 || !q_pos || !out_bf16) return fail(RKV_EINVAL, "null tensor pointer");
+  if (!aligned(k_bf16, 16) || !aligned(v_bf16, 16)) return fail(RKV_EINVAL, "k/v must be 16-byte aligned");
+  if (!aligned(q_bf16, 16) || !aligned(out_bf16, 16))
+    return fail(RKV_EINVAL, "q/out must be 16-byte aligned");
+  if (!aligned(pos, 4) || !aligned(q_pos, 4)) return fail(RKV_EINVAL, "pos/q_pos must be 4-byte aligned");
+  if (n < 1 || n > c->p.n_slots)
+    return fail(RKV_EINVAL, "n = " + std::to_string(n) + " outside [1, n_slots]");
+  if (n_q < 1 || n_q > c->p.max_queries)
+    return fail(RKV_EINVAL, "n_q = " + std::to_string(n_q) + " outside [1, max_queries]");
+  hipError_t e = rkv::launch_write_attend(c->g, c->ws, layer, k_bf16, v_bf16, pos, n, q_bf16, q_pos, n_q,
+                                          out_bf16, stream);
+  if (e != hipSuccess) return hip_fail(e, "write/attend kernel launch");
+  return RKV_OK;
+}
+
 }  // extern "C"

@@ -36,5 +36,19 @@ hipError_t launch_rotate(const Geom& g, int layer_lo, int layer_hi, int32_t delt
                          const float* cosv, const float* sinv, hipStream_t s);
 hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void* q,
                          const int32_t* q_pos, int n_q, void* out, hipStream_t s);
+// Write, then attention, with the query preparation in the write's launch.
+hipError_t launch_write_attend(const Geom& g, const AttnWs& ws, int layer, const void* k, const void* v,
+                               const int32_t* pos, int n, const void* q, const int32_t* q_pos, int n_q,
+                               void* out, hipStream_t s);
+
+// Grid of the write: `groups` 16-slot groups (a run of n slots meets at most
+// n/16 + 2 of them) times n_heads / hg head groups of hg heads.
+inline void write_grid(const Geom& g, int n, int* groups, int* hg) {
+  const int NG = (g.n_slots + 15) / 16;
+  *groups = (n + 15) / 16 + 2;
+  if (*groups > NG) *groups = NG;
+  const int H = g.n_heads;
+  *hg = H % 4 == 0 ? 4 : (H % 2 == 0 ? 2 : 1);
+}
 
 }  // namespace rkv

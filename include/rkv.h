@@ -159,6 +159,18 @@ int cache_delta_rotate(rkv_cache* c, int32_t layer, int32_t delta, hipStream_t s
 int cache_attend(rkv_cache* c, int32_t layer, const void* q_bf16, const int32_t* q_pos,
                  int32_t n_q, void* out_bf16, hipStream_t stream);
 
+/* One call of the per-chunk sequence (§2 "The step budget", Appendix G: each
+ * call writes its new chunk, then attends over the whole cache):
+ * cache_write_rope_fp8(k, v, pos, n) followed by cache_attend(q, q_pos,
+ * n_q, out), with the same arguments, results, requirements and errors
+ * (checked before anything is enqueued).  For head_dim 128 the queries are
+ * prepared in the write's launch, one launch fewer than the two calls.
+ * Reads of q may not overlap the cache's own writes of this call: q, k, v
+ * and out are distinct tensors. */
+int cache_write_attend(rkv_cache* c, int32_t layer, const void* k_bf16, const void* v_bf16,
+                       const int32_t* pos, int32_t n, const void* q_bf16, const int32_t* q_pos,
+                       int32_t n_q, void* out_bf16, hipStream_t stream);
+
 /* Message for the last error on the calling thread ("" if none). */
 const char* rkv_last_error(void);
 

@@ -1,0 +1,97 @@
+"""cache_write_attend (one call: write the chunk, then attend) against the
+two calls it stands for, through the C ABI.
+
+The per-call sequence of the Runway Characters paper (§2 "The step budget",
+Appendix G) writes each new chunk and then attends over the whole cache.
+The fused entry point prepares the queries in the write's launch; it must
+leave the cache, the ring state and the output bit-identical to
+cache_write_rope_fp8 followed by cache_attend, on every head-group shape of
+the write (4, 2 or 1 heads per workgroup), both precisions, D = 64 (two
+launches) and a wrapping ring.  The output is also gated against the
+oracle of the kernel's declared numerics.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_ring_kv_amd as rkv
+from oracle import attend as oatt, ring as oring
+from oracle.bf16 import round_bf16
+from tests.gpu_common import DEV, attn_errors, pos_dev, require_gpu, to_dev
+from workloads import Config, OutlierSpec, Stream, positions
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+@pytest.mark.parametrize("n_heads,head_dim,precision", [
+    (12, 128, rkv.RKV_PRECISE),  # 4 heads per write workgroup
+    (6, 128, rkv.RKV_PRECISE),   # 2
+    (3, 128, rkv.RKV_PRECISE),   # 1
+    (12, 128, rkv.RKV_FAST),     # single-term precision
+    (4, 64, rkv.RKV_PRECISE),    # D = 64: write launch, then the attention call
+])
+def test_write_attend_equals_write_then_attend(n_heads, head_dim, precision):
+    n_slots, chunk = 1000, 300
+    cfg = Config("wa", n_heads=n_heads, head_dim=head_dim, n_slots=n_slots, chunk=chunk, seed=31,
+                 outliers=OutlierSpec(0.02, 8.0))
+    mk = lambda: rkv.RingCache(1, n_slots, n_heads, head_dim, chunk, precision, device=DEV)
+    fused, split = mk(), mk()
+    st = oring.RingState(n_slots, n_heads, head_dim)
+    s = Stream(cfg)
+    for c in range(5):  # 1,500 tokens into 1,000 slots: the ring wraps
+        q, k, v = s.chunk()
+        pos = positions(chunk * c, chunk)
+        kd, vd, qd, pd = to_dev(k), to_dev(v), to_dev(q), pos_dev(pos)
+        out_f = fused.write_attend(0, kd, vd, pd, qd, pd)
+        split.write(0, kd, vd, pd)
+        out_s = split.attend(0, qd, pd)
+        oring.write(st, k.f64, v.f64, pos)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out_f), _bits(out_s)), f"chunk {c}: output differs"
+        assert fused.state(0)[:2].cpu().tolist() == split.state(0)[:2].cpu().tolist()
+        for a, b in zip(fused.codes(0) + fused.scales(0), split.codes(0) + split.scales(0)):
+            assert torch.equal(a, b), f"chunk {c}: cache differs"
+        assert torch.equal(fused.slot_pos(0), split.slot_pos(0))
+        assert torch.equal(fused.vmax(0), split.vmax(0))
+    if precision == rkv.RKV_PRECISE:
+        # against the oracle of the kernel's declared numerics (fp64 on the
+        # dequantized cache), normalized per output channel.  (The fast mode's
+        # single-term probabilities are gated on unit-normal data elsewhere;
+        # here it is checked for equivalence only.)
+        out = out_f.float().cpu().numpy().astype(np.float64)
+        em = round_bf16(oatt.attend_emul(st, q.f64, pos))
+        _, _, nmax, nmean = attn_errors(out, em, oatt.sigma_v(st))
+        assert nmax < 2e-2 and nmean < 2e-3, (nmax, nmean)
+
+
+def test_write_attend_rejects_bad_arguments():
+    cache = rkv.RingCache(1, 64, 1, 128, 16, device=DEV)
+    z = lambda n: torch.zeros(n, 1, 128, dtype=torch.bfloat16, device=DEV)
+    p = lambda n: torch.zeros(n, dtype=torch.int32, device=DEV)
+    h = cache.handle
+    cases = [
+        (z(65), z(65), p(65), z(4), p(4), 65, 4),   # n > n_slots
+        (z(4), z(4), p(4), z(17), p(17), 4, 17),    # n_q > max_queries
+        (z(4), z(4), p(4), z(4), p(4), 0, 4),       # n = 0
+        (z(4), z(4), p(4), z(4), p(4), 4, 0),       # n_q = 0
+    ]
+    out = z(17)
+    for k, v, pos, q, qp, n, n_q in cases:
+        with pytest.raises(rkv.RkvError) as e:
+            rkv.cache_write_attend(h, 0, k.data_ptr(), v.data_ptr(), pos.data_ptr(), n, q.data_ptr(),
+                                   qp.data_ptr(), n_q, out.data_ptr(), 0)
+        assert e.value.code == rkv.RKV_EINVAL
+    with pytest.raises(rkv.RkvError):
+        rkv.cache_write_attend(h, 1, z(4).data_ptr(), z(4).data_ptr(), p(4).data_ptr(), 4, z(4).data_ptr(),
+                               p(4).data_ptr(), 4, out.data_ptr(), 0)  # no layer 1
+    torch.cuda.synchronize()
+    assert cache.state(0)[:2].cpu().tolist() == [0, 0]  # nothing was enqueued
