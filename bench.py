@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--precision", choices=["precise", "fast"], default="precise")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--attend-components-only", action="store_true",
+                    help="of the per-operation loops, run only the attention call's (counter runs)")
     ap.add_argument("--reps", type=int, default=200, help="launches per component loop")
     ap.add_argument("--workgroups", type=int, default=0,
                     help="persistent workgroups per attention call (0 = one per compute unit)")
@@ -267,15 +269,16 @@ def main():
         q0, k0, v0 = pool[0]
         comp["attend_us"] = 1e3 * timed(lambda: cache.attend(0, q0, pos_pool[0], out), r, stream)
         comp["write_us"] = 1e3 * timed(lambda: cache.write(0, k0, v0, pos_pool[0]), r, stream)
+        comp["attend_TFLOPs"] = ATTN_FLOP / comp["attend_us"] / 1e6
+        comp["write_GBps"] = WRITE_BYTES / comp["write_us"] / 1e3
+    if not args.no_components and not args.attend_components_only:
         flip = [1]
 
         def rot():
             cache.rotate(0, flip[0])
             flip[0] = -flip[0]
         comp["rotate_1layer_us"] = 1e3 * timed(rot, max(20, r // 4), stream)
-        comp["write_GBps"] = WRITE_BYTES / comp["write_us"] / 1e3
         comp["rotate_1layer_GBps"] = ROTATE_BYTES / comp["rotate_1layer_us"] / 1e3
-        comp["attend_TFLOPs"] = ATTN_FLOP / comp["attend_us"] / 1e6
         # 60 stacked layer caches (1.1 GB): rotation of every layer in one launch,
         # and writes cycling over the layers -- both far beyond the 256 MB cache
         big = rkv.RingCache(60, N, H, D, CHUNK, prec, device=dev)
@@ -323,6 +326,7 @@ def main():
     }
     if comp:
         res["components"] = {k: round(v, 4) for k, v in comp.items()}
+    if "attend_us" in comp:
         res["write_GBps"] = round(comp["write_GBps"], 2)
         achieved = comp["attend_TFLOPs"]
         res["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2),
@@ -331,6 +335,7 @@ def main():
                            "kernel": "cache_attend call = q_prep_kernel + attend_kernel",
                            "per_launch_flop": ATTN_FLOP,
                            "per_launch_us": round(comp["attend_us"], 3)}
+    if "rotate_60layer_GBps" in comp:
         res["roofline_hbm"] = {
             "write": {"achieved": round(comp["write_GBps"], 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                       "frac": round(comp["write_GBps"] / PEAK_HBM_GBPS, 4), "bytes": WRITE_BYTES},
