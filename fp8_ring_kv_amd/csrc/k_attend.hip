@@ -370,7 +370,9 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
     }
     // (the low-half conversion keeps the high half of its third operand,
     // which the high-half conversion overwrites: any value will do)
-    uint32_t hw = pack2_fp8<false>(x[0], x[1], __builtin_nondeterministic_value(0u));
+    uint32_t blank;  // an opaque value (the asm defines it), so no copy is needed
+    asm volatile("" : "=v"(blank));
+    uint32_t hw = pack2_fp8<false>(x[0], x[1], blank);
     hw = pack2_fp8<true>(x[2], x[3], hw);
     ph[w] = (int)hw;
     if (TERMS == 2) {  // second term: 16 (x - e4m3(x)), descaled by 2^-4
@@ -813,11 +815,16 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
       read_k<D>(kf, lb, off);
       qk<D, TERMS>(sacc, kf, qf, qs);
       read_v<D>(vf, lb, off);
+      // Only the first and last tiles of the valid range and the ring's last
+      // tile (pad slots) can hold invalid slots: the others skip the mask.
       const int T = tile_of(t_lo + j);
-      const int sl = T * kTile + lane;
-      int rel = sl - a;
-      if (rel < 0) rel += N;
-      const unsigned long long mask = __ballot(sl < N && rel < nv);
+      unsigned long long mask = ~0ull;
+      if (t_lo + j == 0 || t_lo + j == count - 1 || T == NT - 1) {
+        const int sl = T * kTile + lane;
+        int rel = sl - a;
+        if (rel < 0) rel += N;
+        mask = __ballot(sl < N && rel < nv);
+      }
       softmax_pv<D, TERMS>(sacc, vf, st, mask, l2c, lane, lb + off.sk4);
     }
 
