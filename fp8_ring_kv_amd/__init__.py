@@ -279,7 +279,7 @@ class RingCache:
         """(head, n_valid, ...) int32 on device (entries past the first two are
         counters internal to the write kernel)."""
         lay = self.layout(layer)
-        return self._view(lay.state, 48, torch.int32)
+        return self._view(lay.state, 16, torch.int32)
 
     def vmax(self, layer: int) -> torch.Tensor:
         """[H] float32: largest value scale written to each head since the reset."""

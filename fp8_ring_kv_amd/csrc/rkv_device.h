@@ -12,10 +12,10 @@ namespace rkv {
 constexpr float kE4M3Max = 448.0f;
 constexpr int kTile = 64;        // slots per attention tile and per V transpose tile
 constexpr int kMaxHalfDim = 64;  // D/2 for the largest supported head_dim (128)
-// Per-layer counters and maxima are spread over kSub slots so that no single
+// Per-head value-scale maxima are spread over kSub slots so that no single
 // address takes more than a fraction of one launch's atomics.
 constexpr int kSub = 8;
-constexpr int kStateInts = 4 + kSub;  // head, n_valid, top counter, 0, sub-counters
+constexpr int kStateInts = 4;  // head, n_valid, write ticket counter, 0
 
 // Byte offsets of one layer's arrays (relative to the layer's start) and the
 // sizes every kernel needs.  Passed by value as a kernel argument.
@@ -35,7 +35,7 @@ struct LayerPtrs {
   float* scale_k;
   float* scale_v;
   int32_t* slot_pos;
-  int32_t* state;  // {head, n_valid, top counter, 0, sub-counters[kSub]}
+  int32_t* state;  // {head, n_valid, write ticket counter, 0}
   uint32_t* vmax;  // [H][kSub] largest value scale written since the reset (fp32
                    // bits); the head's bound is the max over its kSub entries
 };

@@ -60,22 +60,6 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
     }
     p = pos[i];
   }
-  // Tickets for the device-side write position, taken once head and n_valid
-  // are read (and after the row loads are issued: a returning atomic holds
-  // up every later load's wait): whoever takes the last ticket knows every
-  // workgroup has read them and may advance them.  Workgroup w takes a ticket on
-  // sub-counter w % kSub; the last arrival of each sub-group takes one on the
-  // top counter, so no counter sees more than ceil(total / kSub) atomics.
-  // The increment depends on the loaded head (it is always 1), so it cannot
-  // be issued before the load returns.  No workgroup reads what another one
-  // writes, so relaxed device-scope atomics suffice; the next kernel on the
-  // stream sees the new state.
-  // (The returned ticket is looked at only at the end of the kernel.)
-  const int wg = (int)(by * gx + bx);
-  int t1 = 0;
-  if (threadIdx.x == 0)
-    t1 = __hip_atomic_fetch_add(&L.state[4 + wg % kSub], head < 0x7FFFFFFF ? 1 : 2, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
   // angles for every lane (the table index is always in range; inactive
   // lanes rotate zeros), so the four table loads issue together
   float cs[4], sn[4];
@@ -176,21 +160,21 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, vmx[threadIdx.x][e]);
     if (mx > 0.f) atomicMax(&L.vmax[(h0 + threadIdx.x) * kSub + bx % kSub], __float_as_uint(mx));
   }
-  // The last arrival of each sub-group takes a ticket on the top counter;
-  // the last of those advances the write position.
+  // Ticket for the device-side write position: each workgroup takes one as
+  // it finishes, long after it read head and n_valid, so whoever takes the
+  // last ticket knows every workgroup has read them and may advance them.
+  // The tickets arrive spread over the workgroups' finishing times, on one
+  // counter.  The increment depends on the loaded head (it is always 1).  No
+  // workgroup reads what another one writes, so relaxed device-scope atomics
+  // suffice; the next kernel on the stream sees the new state.
   if (threadIdx.x == 0) {
-    const int total = (int)(gx * gy);
-    const int k = wg % kSub;
-    const int ksize = (total - k + kSub - 1) / kSub;  // workgroups with wg % kSub == k
-    const int nsub = total < kSub ? total : kSub;
-    if (t1 == ksize - 1) {
-      __hip_atomic_store(&L.state[4 + k], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int t2 = __hip_atomic_fetch_add(&L.state[2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (t2 == nsub - 1) {
-        __hip_atomic_store(&L.state[2], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        L.state[0] = (int)(((long long)head + n) % N);
-        L.state[1] = nvalid + n < N ? nvalid + n : N;
-      }
+    const int total = gx * gy;
+    const int t = __hip_atomic_fetch_add(&L.state[2], head < 0x7FFFFFFF ? 1 : 2, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    if (t == total - 1) {
+      __hip_atomic_store(&L.state[2], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      L.state[0] = (int)(((long long)head + n) % N);
+      L.state[1] = nvalid + n < N ? nvalid + n : N;
     }
   }
 }
