@@ -29,6 +29,9 @@ FLAGS = [
     # no value here is ever NaN: min/max need no quieting of their inputs
     # (infinities keep their meaning: -inf marks masked slots)
     "-fno-honor-nans",
+    # every atomic here is issued by one lane: no wave-level aggregation, whose
+    # broadcast of the returned value would wait for it on the spot
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

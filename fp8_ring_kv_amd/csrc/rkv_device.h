@@ -69,33 +69,60 @@ __device__ inline uint32_t f32_to_bf16_rne(float x) {
   return u >> 16;
 }
 
-__device__ inline float clamp448(float x) { return fminf(fmaxf(x, -kE4M3Max), kE4M3Max); }
+// fp32(x / 448), correctly rounded, for x >= 0: the product with the
+// rounded reciprocal, corrected once by its exact residual.  An exhaustive
+// comparison with the division over every normal fp32 x gives identical
+// results wherever the quotient is a normal number; below that (x < 2^-117)
+// the division itself is taken, on a branch that is skipped unless a lane
+// needs it.
+__device__ inline float div448(float x) {
+  constexpr float c = 1.f / kE4M3Max;
+  const float q0 = x * c;
+  float q = fmaf(fmaf(-q0, kE4M3Max, x), c, q0);
+  if (__builtin_expect(x < 0x1p-117f, 0)) q = x / kE4M3Max;
+  return q;
+}
 
-// e4m3(y / s) exactly as rounding the true quotient would give it, returned
-// as an fp32 value the hardware RNE conversion maps to the right code.
-// q = RN(y / s) (y * r with one Newton correction, r = 1/s).  The e4m3 grid
-// and its midpoints are fp32 values, so RNE(q) equals RNE(y / s) unless q sits
-// exactly on a midpoint while y / s does not (y / s within half an fp32 ulp of
-// it -- frequent with bf16 inputs, whose quotients by the rounded scale land
-// next to midpoints).  Then the sign of the exact residual y - q s (one fma)
-// says which side y / s is on, and q moves one fp32 ulp that way.
-__device__ inline float quant_div(float y, float s, float r) {
-  float q = y * r;
-  q = fmaf(fmaf(-q, s, y), r, q);
-  const float res = fmaf(-q, s, y);
-  const uint32_t b = __float_as_uint(q);
-  const uint32_t a = b & 0x7FFFFFFFu;
-  // midpoint test: normal e4m3 range (|q| >= 2^-6): the 20 fp32 mantissa bits
-  // below the 3 e4m3 ones are 1000...0; subnormal range: 1024 |q| is odd.
-  // Evaluated without short-circuits so that it compiles to selects.
-  const float t = __uint_as_float(a) * 1024.f;
-  const bool normal = a >= 0x3C800000u;
-  const bool mid_n = (a & 0xFFFFFu) == 0x80000u;
-  const bool mid_s = (t == rintf(t)) & ((((int)t) & 1) != 0);
-  const bool adj = (normal ? mid_n : mid_s) & (res != 0.f);
-  const uint32_t step = ((res > 0.f) == (q > 0.f)) ? 1u : 0xFFFFFFFFu;
-  q = __uint_as_float(b + (adj ? step : 0u));
-  return clamp448(q);
+// 1/s for a scale s (0 for s = 0: an all-zero row quantizes to zero codes).
+// One hardware reciprocal (within 1 ulp).  Scales below the fp32 normal
+// range (amax * margin < 448 * 2^-126, about 5e-36) are outside the
+// supported input range and quantize to zero codes.
+__device__ inline float recip_scale(float s) { return s >= 0x1p-126f ? __builtin_amdgcn_rcpf(s) : 0.f; }
+
+// Per-row constants of the exact quotient code e4m3(y / s) for bf16 values y
+// with s = fp32(am / 448), am = fp32(amax * margin) holding a bf16 amax times
+// a margin whose product is exact (1.0, 1.5).
+//   y / s = R / (1 + delta), with R = 448 y / am and s = (am / 448)(1 + delta).
+//   With 8-bit significands in y and amax, R is either an e4m3 midpoint
+//   exactly or at least 1/(mantissa(am) * 31) >= 1.2e-4 (relative) from every
+//   midpoint (midpoints have at most 5 significant bits).  So the code of
+//   y / s is the code of R unless R is a midpoint, and then the sign of delta,
+//   one value per row, decides: delta > 0 puts y / s below the midpoint in
+//   magnitude, delta < 0 above, delta = 0 (s exact) leaves an exact tie that
+//   goes to the even code.
+//   Per element: q = y / s rounded to fp32 within about an ulp (the product
+//   with 1/s plus one Newton correction, exact when y / s is representable),
+//   then scaled by f = 1 -/+ 2^-20 when delta is positive/negative: far more
+//   than q's error or |delta| (<= 2^-24), far less than the 1.2e-4 gap, so
+//   every near-midpoint quotient lands on the side delta says and no other
+//   code changes.  The hardware RNE conversion of the clamped result is the
+//   code.  Checked on the host against an exact reference for every bf16
+//   amax of one binade and every bf16 y with |y| <= amax, margins 1 and 1.5,
+//   with the reciprocal exact or one ulp off either way.
+struct VQuot {
+  float s, r, f;
+};
+__device__ inline VQuot vquot_row(float am, float s) {
+  VQuot c;
+  c.s = s;
+  c.r = recip_scale(s);
+  const float e = fmaf(s, kE4M3Max, -am);  // the sign of delta, exactly
+  c.f = e > 0.f ? 1.f - 0x1p-20f : (e < 0.f ? 1.f + 0x1p-20f : 1.f);
+  return c;
+}
+__device__ inline float quant_v(float y, const VQuot& c) {
+  const float q0 = y * c.r;
+  return __builtin_amdgcn_fmed3f(fmaf(fmaf(-q0, c.s, y), c.r, q0) * c.f, -kE4M3Max, kE4M3Max);
 }
 
 // Two fp32 values -> two e4m3fn codes (round to nearest even) placed in the

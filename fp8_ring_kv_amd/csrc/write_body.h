@@ -60,12 +60,35 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
     }
     p = pos[i];
   }
-  // angles for every lane (the table index is always in range; inactive
-  // lanes rotate zeros), so the four table loads issue together
-  float cs[4], sn[4];
+  // Ticket for the device-side write position, one per workgroup on one
+  // counter, taken once head and n_valid are read (the increment depends on
+  // the loaded head; it is always 1).  Whoever takes the last ticket knows
+  // that every workgroup has read the position and may advance it.  No
+  // workgroup reads what another writes: relaxed device-scope atomics
+  // suffice; the next kernel on the stream sees the new state.
+  // The ticket goes out once every load of this workgroup has returned (the
+  // frequency table included): vector memory operations complete in order, so
+  // a wait for a load issued after the ticket, or one the compiler cannot
+  // place relative to it, would wait for its round trip too.  Issued here, it
+  // returns while the arithmetic below runs.
+  double tw[4];
   const double* turns = omega_turns(g);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) rope_cs(p, turns[4 * lane + m], cs[m], sn[m]);
+  for (int m = 0; m < 4; ++m) tw[m] = turns[4 * lane + m];
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh)
+    asm volatile("" ::"v"(kw[hh].x), "v"(kw[hh].y), "v"(kw[hh].z), "v"(kw[hh].w), "v"(vw[hh].x), "v"(vw[hh].y),
+                 "v"(vw[hh].z), "v"(vw[hh].w));
+  asm volatile("" ::"v"(p), "v"(tw[0]), "v"(tw[1]), "v"(tw[2]), "v"(tw[3]) : "memory");
+  int ticket = -1;
+  if (threadIdx.x == 0)
+    ticket = __hip_atomic_fetch_add(&L.state[2], head < 0x7FFFFFFF ? 1 : 2, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+  // angles for every lane (the table index is always in range; inactive
+  // lanes rotate zeros)
+  float cs[4], sn[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) rope_cs(p, tw[m], cs[m], sn[m]);
 
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh) {
@@ -84,21 +107,23 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
     }
     ak = group_max<LPR>(ak);
     av = group_max<LPR>(av);
-    // scale s = fp32(margin * amax / 448); codes = e4m3(y / s)
-    const float sk = ak * g.margin / kE4M3Max, sv = av * g.margin / kE4M3Max;
-    const float rk = sk > 0.f ? 1.f / sk : 0.f;
-    const float rv = sv > 0.f ? 1.f / sv : 0.f;
-    // keys are fp32 RoPE results (a rounding away from the exact rotation
-    // already), values are raw bf16 whose quotients often sit on e4m3 midpoints
+    // scale s = fp32(margin * amax / 448); codes = e4m3(y / s).  Keys are
+    // fp32 RoPE results (a rounding away from the exact rotation already):
+    // y * (1/s).  Values are raw bf16, whose quotients often sit next to e4m3
+    // midpoints: the exact quotient code (vquot_row).
+    const float amk = ak * g.margin, amv = av * g.margin;
+    const float sk = div448(amk), sv = div448(amv);
+    const float rk = recip_scale(sk);
+    const VQuot qv = vquot_row(amv, sv);
     uint2 ck, cv;
     ck.x = pack2_fp8<false>(quant_mul(y[0], rk), quant_mul(y[1], rk), 0u);
     ck.x = pack2_fp8<true>(quant_mul(y[2], rk), quant_mul(y[3], rk), ck.x);
     ck.y = pack2_fp8<false>(quant_mul(y[4], rk), quant_mul(y[5], rk), 0u);
     ck.y = pack2_fp8<true>(quant_mul(y[6], rk), quant_mul(y[7], rk), ck.y);
-    cv.x = pack2_fp8<false>(quant_div(u[0], sv, rv), quant_div(u[1], sv, rv), 0u);
-    cv.x = pack2_fp8<true>(quant_div(u[2], sv, rv), quant_div(u[3], sv, rv), cv.x);
-    cv.y = pack2_fp8<false>(quant_div(u[4], sv, rv), quant_div(u[5], sv, rv), 0u);
-    cv.y = pack2_fp8<true>(quant_div(u[6], sv, rv), quant_div(u[7], sv, rv), cv.y);
+    cv.x = pack2_fp8<false>(quant_v(u[0], qv), quant_v(u[1], qv), 0u);
+    cv.x = pack2_fp8<true>(quant_v(u[2], qv), quant_v(u[3], qv), cv.x);
+    cv.y = pack2_fp8<false>(quant_v(u[4], qv), quant_v(u[5], qv), 0u);
+    cv.y = pack2_fp8<true>(quant_v(u[6], qv), quant_v(u[7], qv), cv.y);
     if (active) {
       const size_t r = (size_t)(h0 + hh) * NP + slot;
       *reinterpret_cast<uint2*>(L.codes_k + r * D + 8 * lane) = ck;
@@ -160,22 +185,12 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, vmx[threadIdx.x][e]);
     if (mx > 0.f) atomicMax(&L.vmax[(h0 + threadIdx.x) * kSub + bx % kSub], __float_as_uint(mx));
   }
-  // Ticket for the device-side write position: each workgroup takes one as
-  // it finishes, long after it read head and n_valid, so whoever takes the
-  // last ticket knows every workgroup has read them and may advance them.
-  // The tickets arrive spread over the workgroups' finishing times, on one
-  // counter.  The increment depends on the loaded head (it is always 1).  No
-  // workgroup reads what another one writes, so relaxed device-scope atomics
-  // suffice; the next kernel on the stream sees the new state.
-  if (threadIdx.x == 0) {
-    const int total = gx * gy;
-    const int t = __hip_atomic_fetch_add(&L.state[2], head < 0x7FFFFFFF ? 1 : 2, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    if (t == total - 1) {
-      __hip_atomic_store(&L.state[2], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      L.state[0] = (int)(((long long)head + n) % N);
-      L.state[1] = nvalid + n < N ? nvalid + n : N;
-    }
+  // The workgroup that took the last ticket advances the device-side write
+  // position (every workgroup had read it before taking its ticket).
+  if (threadIdx.x == 0 && ticket == gx * gy - 1) {
+    __hip_atomic_store(&L.state[2], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    L.state[0] = (int)(((long long)head + n) % N);
+    L.state[1] = nvalid + n < N ? nvalid + n : N;
   }
 }
 

@@ -72,6 +72,31 @@ def test_hardware_e4m3_rounding_is_nearest_even_on_every_midpoint():
     assert np.array_equal(got[~zero], want[~zero]) and np.all((got[zero] & 0x7F) == 0)
 
 
+@pytest.mark.parametrize("margin", [1.0, 1.5])
+def test_value_codes_and_scales_bit_exact(margin):
+    """Values are bf16 and their amax times the margin is exact for margins 1
+    and 1.5, so the stored value scales equal the oracle's fp32(margin amax /
+    448) and every value code is the exact quotient's RNE code, ties included
+    (outlier channels x8 put many quotients next to e4m3 midpoints)."""
+    cfg = Config("vexact", n_heads=4, head_dim=128, n_slots=700, chunk=500, seed=11,
+                 outliers=OutlierSpec(0.05, 8.0))
+    cache = rkv.RingCache(1, cfg.n_slots, cfg.n_heads, cfg.head_dim, 64, rkv.RKV_PRECISE,
+                          cfg.rope_base, margin, device=DEV)
+    st = oring.RingState(cfg.n_slots, cfg.n_heads, cfg.head_dim, cfg.rope_base, margin)
+    s = Stream(cfg)
+    for c in range(3):  # 1,500 tokens into 700 slots: every slot rewritten, the ring wraps
+        _, k, v = s.chunk()
+        pos = positions(500 * c, 500)
+        cache.write(0, to_dev(k), to_dev(v), pos_dev(pos))
+        oring.write(st, k.f64, v.f64, pos)
+    (head, nv), _, _, cv, _, sv = readback(cache, 0)
+    assert (head, nv) == (st.head, st.n_valid)
+    assert np.array_equal(sv[:, : cfg.n_slots], st.scale_v)
+    got, want = cv[:, : cfg.n_slots], st.codes_v
+    zero = (want & 0x7F) == 0  # the sign of a zero code is not kept
+    assert np.array_equal(got[~zero], want[~zero]) and np.all((got[zero] & 0x7F) == 0)
+
+
 @pytest.mark.parametrize("head_dim", [64, 128])
 def test_wrapping_writes_of_varied_sizes(head_dim):
     """Random write sizes (1 .. N, including a full-ring write) wrap the ring many times."""
