@@ -1021,8 +1021,7 @@ hipError_t launch_write_attend(const Geom& g, const AttnWs& ws, int layer, const
   write_grid(g, n, &W.wgx, &hg);
   W.wgy = g.n_heads / hg;
   const int blocks = W.wgx * W.wgy + prep_blocks(W.P);
-  if (hg == 4) launch_write_prep_t<4>(W, blocks, ws.terms, s);
-  else if (hg == 2) launch_write_prep_t<2>(W, blocks, ws.terms, s);
+  if (hg == 2) launch_write_prep_t<2>(W, blocks, ws.terms, s);
   else launch_write_prep_t<1>(W, blocks, ws.terms, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

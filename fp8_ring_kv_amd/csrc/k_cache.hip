@@ -90,12 +90,10 @@ hipError_t launch_write(const Geom& g, int layer, const void* k, const void* v, 
   int groups, hg;
   write_grid(g, n, &groups, &hg);
   if (g.head_dim == 128) {
-    if (hg == 4) launch_write_t<128, 4>(g, layer, k, v, pos, n, groups, s);
-    else if (hg == 2) launch_write_t<128, 2>(g, layer, k, v, pos, n, groups, s);
+    if (hg == 2) launch_write_t<128, 2>(g, layer, k, v, pos, n, groups, s);
     else launch_write_t<128, 1>(g, layer, k, v, pos, n, groups, s);
   } else {
-    if (hg == 4) launch_write_t<64, 4>(g, layer, k, v, pos, n, groups, s);
-    else if (hg == 2) launch_write_t<64, 2>(g, layer, k, v, pos, n, groups, s);
+    if (hg == 2) launch_write_t<64, 2>(g, layer, k, v, pos, n, groups, s);
     else launch_write_t<64, 1>(g, layer, k, v, pos, n, groups, s);
   }
   return hipGetLastError();

@@ -42,13 +42,15 @@ hipError_t launch_write_attend(const Geom& g, const AttnWs& ws, int layer, const
                                void* out, hipStream_t s);
 
 // Grid of the write: `groups` 16-slot groups (a run of n slots meets at most
-// n/16 + 2 of them) times n_heads / hg head groups of hg heads.
+// n/16 + 2 of them) times n_heads / hg head groups of hg heads.  Two heads per
+// workgroup: the write is bound by each wave's arithmetic latency, and 4 heads
+// per workgroup ran 0.5 us slower (fewer, longer waves over the compute units).
 inline void write_grid(const Geom& g, int n, int* groups, int* hg) {
   const int NG = (g.n_slots + 15) / 16;
   *groups = (n + 15) / 16 + 2;
   if (*groups > NG) *groups = NG;
   const int H = g.n_heads;
-  *hg = H % 4 == 0 ? 4 : (H % 2 == 0 ? 2 : 1);
+  *hg = H % 2 == 0 ? 2 : 1;
 }
 
 }  // namespace rkv

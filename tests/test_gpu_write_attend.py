@@ -6,7 +6,7 @@ Appendix G) writes each new chunk and then attends over the whole cache.
 The fused entry point prepares the queries in the write's launch; it must
 leave the cache, the ring state and the output bit-identical to
 cache_write_rope_fp8 followed by cache_attend, on every head-group shape of
-the write (4, 2 or 1 heads per workgroup), both precisions, D = 64 (two
+the write (2 or 1 heads per workgroup), both precisions, D = 64 (two
 launches) and a wrapping ring.  The output is also gated against the
 oracle of the kernel's declared numerics.
 """
@@ -33,9 +33,9 @@ def _bits(t: torch.Tensor) -> torch.Tensor:
 
 
 @pytest.mark.parametrize("n_heads,head_dim,precision", [
-    (12, 128, rkv.RKV_PRECISE),  # 4 heads per write workgroup
-    (6, 128, rkv.RKV_PRECISE),   # 2
-    (3, 128, rkv.RKV_PRECISE),   # 1
+    (12, 128, rkv.RKV_PRECISE),  # 2 heads per write workgroup, 6 head groups
+    (6, 128, rkv.RKV_PRECISE),   # 2 heads, 3 groups
+    (3, 128, rkv.RKV_PRECISE),   # 1 head per workgroup
     (12, 128, rkv.RKV_FAST),     # single-term precision
     (4, 64, rkv.RKV_PRECISE),    # D = 64: write launch, then the attention call
 ])
