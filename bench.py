@@ -154,6 +154,30 @@ def cpu_baseline():
     }
 
 
+def measured_peaks(stream):
+    """The two ceilings measured on this device with the library's probes
+    (include/rkv_probe.h), reported beside the published peaks: dense FP8
+    matrix throughput of the attention's instruction, and the HBM bandwidth
+    of an in-place streaming read-modify-write (the rotation's pattern) over
+    1 GiB, far beyond the 256 MB last-level cache (best of three timings)."""
+    import torch
+    import fp8_ring_kv_amd as rkv
+    s = stream.cuda_stream
+    wg, iters = 2048, 2000
+    sink = torch.empty(wg, dtype=torch.float32, device="cuda:0")
+    rkv.rkv_probe_fp8_mfma(wg, 10, sink.data_ptr(), s)  # warm-up (code load)
+    ms = timed(lambda: rkv.rkv_probe_fp8_mfma(wg, iters, sink.data_ptr(), s), 5, stream)
+    mfma_tflops = wg * 4 * iters * 4 * 131072 / ms / 1e9
+    nbytes = 1 << 30
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    rkv.rkv_probe_stream(buf.data_ptr(), nbytes, s)  # warm-up
+    ms = min(timed(lambda: rkv.rkv_probe_stream(buf.data_ptr(), nbytes, s), 4, stream) for _ in range(3))
+    del buf, sink
+    return {"fp8_mfma_TFLOPs": round(mfma_tflops, 1), "hbm_stream_GBps": round(2 * nbytes / ms / 1e6, 1),
+            "probes": "rkv_probe_fp8_mfma (2048 x 4 waves x 2000 x 4 instructions 32x32x64 e4m3), "
+                      "rkv_probe_stream (in-place read-modify-write of 1 GiB, 2 GiB moved)"}
+
+
 def graph_step_ms(args, cache, pool, pos_pool, out, stream):
     """The bench steps captured once as HIP graphs (one per step of the reset
     period, the rotation in the first) and replayed, continuing the eager step
@@ -262,6 +286,7 @@ def main():
         del src, dst
 
     comp = {}
+    peaks = None
     if not args.no_graph:
         comp["graph_us_per_step"] = 1e3 * graph_step_ms(args, cache, pool, pos_pool, out, stream)
     if not args.no_components:
@@ -304,6 +329,7 @@ def main():
         comp["write_60layer_cycling_GBps"] = WRITE_BYTES / comp["write_60layer_cycling_us"] / 1e3
         del big
         torch.cuda.synchronize()
+        peaks = measured_peaks(stream)
 
     res = {
         "metric": "µs per attention call (757q×5788 FP8 KV) + cache-write GB/s; % of roofline",
@@ -335,6 +361,8 @@ def main():
                            "kernel": "cache_attend call = q_prep_kernel + attend_kernel",
                            "per_launch_flop": ATTN_FLOP,
                            "per_launch_us": round(comp["attend_us"], 3)}
+        if peaks:
+            res["roofline"]["frac_of_measured_peak"] = round(achieved / peaks["fp8_mfma_TFLOPs"], 4)
     if "rotate_60layer_GBps" in comp:
         res["roofline_hbm"] = {
             "write": {"achieved": round(comp["write_GBps"], 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -343,6 +371,11 @@ def main():
                                "unit": "GB/s", "frac": round(comp["rotate_60layer_GBps"] / PEAK_HBM_GBPS, 4),
                                "bytes": 60 * ROTATE_BYTES},
         }
+        if peaks:
+            for part in res["roofline_hbm"].values():
+                part["frac_of_measured_peak"] = round(part["achieved"] / peaks["hbm_stream_GBps"], 4)
+    if peaks:
+        res["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline()
     print(json.dumps(res), flush=True)

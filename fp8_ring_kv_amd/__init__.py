@@ -24,7 +24,7 @@ __all__ = [
     "ring_cache_bytes", "ring_cache_create", "ring_cache_destroy", "ring_cache_reset",
     "ring_cache_layout", "cache_write_rope_fp8", "cache_delta_rotate", "cache_attend",
     "cache_write_attend",
-    "rkv_last_error", "RingCache",
+    "rkv_last_error", "rkv_probe_fp8_mfma", "rkv_probe_stream", "RingCache",
 ]
 
 RKV_OK, RKV_EINVAL, RKV_EHIP = 0, -1, -2
@@ -105,6 +105,10 @@ def lib() -> ctypes.CDLL:
     L.cache_write_attend.restype = ctypes.c_int
     L.rkv_last_error.argtypes = []
     L.rkv_last_error.restype = ctypes.c_char_p
+    L.rkv_probe_fp8_mfma.argtypes = [I32, I32, VP, VP]
+    L.rkv_probe_fp8_mfma.restype = ctypes.c_int
+    L.rkv_probe_stream.argtypes = [VP, SZ, VP]
+    L.rkv_probe_stream.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -173,6 +177,20 @@ def cache_write_attend(handle: int, layer: int, k: int, v: int, pos: int, n: int
                                   ctypes.c_void_p(out), ctypes.c_void_p(stream))
     if rc != RKV_OK:
         raise RkvError(rc, "cache_write_attend")
+
+
+# ---- measurement aids (include/rkv_probe.h) ----------------------------------
+
+def rkv_probe_fp8_mfma(workgroups: int, iters: int, sink: int, stream: int) -> None:
+    rc = lib().rkv_probe_fp8_mfma(workgroups, iters, ctypes.c_void_p(sink), ctypes.c_void_p(stream))
+    if rc != RKV_OK:
+        raise RkvError(rc, "rkv_probe_fp8_mfma")
+
+
+def rkv_probe_stream(buf: int, nbytes: int, stream: int) -> None:
+    rc = lib().rkv_probe_stream(ctypes.c_void_p(buf), nbytes, ctypes.c_void_p(stream))
+    if rc != RKV_OK:
+        raise RkvError(rc, "rkv_probe_stream")
 
 
 # ---- torch-facing wrapper ---------------------------------------------------

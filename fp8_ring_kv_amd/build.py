@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "librkv.so")
 OBJ = os.path.join(ROOT, "_build")
-SOURCES = ["rkv_api.cpp", "k_cache.hip", "k_attend.hip"]
+SOURCES = ["rkv_api.cpp", "k_cache.hip", "k_attend.hip", "k_probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -11,14 +11,18 @@ import pytest
 import fp8_ring_kv_amd as rkv
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rkv.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
-    return sorted(set(n for n in names if n not in ("if", "defined")))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text,
+                                flags=re.M))
+    return sorted(n for n in names if n not in ("if", "defined"))
 
 
 def test_library_is_built():
@@ -29,7 +33,8 @@ def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) >= {"ring_cache_bytes", "ring_cache_create", "ring_cache_destroy",
                           "ring_cache_reset", "ring_cache_layout", "cache_write_rope_fp8",
-                          "cache_delta_rotate", "cache_attend", "rkv_last_error"}
+                          "cache_delta_rotate", "cache_attend", "cache_write_attend", "rkv_last_error",
+                          "rkv_probe_fp8_mfma", "rkv_probe_stream"}
     L = rkv.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -100,3 +105,21 @@ def test_calls_on_null_cache_are_einval():
     assert L.ring_cache_reset(None, -1, None) == rkv.RKV_EINVAL
     assert L.ring_cache_layout(None, 0, None) == rkv.RKV_EINVAL
     assert L.ring_cache_destroy(None) == rkv.RKV_OK
+
+
+def test_probes_reject_misuse_without_launching():
+    """The measurement aids validate their arguments on the host: nothing
+    below reaches a kernel launch (no GPU here)."""
+    L = rkv.lib()
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: every call fails validation first
+    assert L.rkv_probe_fp8_mfma(1, 1, None, None) == rkv.RKV_EINVAL
+    assert L.rkv_probe_fp8_mfma(0, 1, fake, None) == rkv.RKV_EINVAL
+    assert L.rkv_probe_fp8_mfma(65537, 1, fake, None) == rkv.RKV_EINVAL
+    assert L.rkv_probe_fp8_mfma(1, 0, fake, None) == rkv.RKV_EINVAL
+    assert L.rkv_probe_fp8_mfma(1, (1 << 20) + 1, fake, None) == rkv.RKV_EINVAL
+    assert L.rkv_probe_fp8_mfma(1, 1, ctypes.c_void_p(0x100002), None) == rkv.RKV_EINVAL
+    assert L.rkv_probe_stream(None, 16, None) == rkv.RKV_EINVAL
+    assert L.rkv_probe_stream(ctypes.c_void_p(0x100008), 16, None) == rkv.RKV_EINVAL
+    assert L.rkv_probe_stream(fake, 0, None) == rkv.RKV_EINVAL
+    assert L.rkv_probe_stream(fake, 24, None) == rkv.RKV_EINVAL
+    assert "multiple of 16" in rkv.rkv_last_error()
