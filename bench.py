@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 H, D, N, CHUNK, RESET_EVERY = 12, 128, 5788, 757, 42
 ATTN_FLOP = 4.0 * CHUNK * N * H * D  # QK^T and PV, 2 flops per multiply-add
+STRESS_FLOP = 4.0 * CHUNK * 11576 * 48 * D  # the stress shape: 48 heads, 11,576 slots
 WRITE_BYTES = (6 * H * D + 8 * H + 4) * CHUNK  # bf16 K,V in; e4m3 K,V + 2 scales + pos out
 ROTATE_BYTES = (2 * H * D + 8 * H + 8) * N  # codes r/w, scale r/w, position r/w
 PEAK_FP8_TFLOPS = 5000.0
@@ -327,7 +328,45 @@ def main():
             lay[0] += 1
         comp["write_60layer_cycling_us"] = 1e3 * timed(wr60, 240, stream)
         comp["write_60layer_cycling_GBps"] = WRITE_BYTES / comp["write_60layer_cycling_us"] / 1e3
+        # per-chunk sequence on the 60 layer caches: 4 denoising passes x 60
+        # layers = 240 attention calls of 757 queries, each layer's cache
+        # written once (the first pass writes and attends in one call); the
+        # reset every 42 chunks is amortized from the 60-layer rotation above
+        ch = [0]
+
+        def chunk60():
+            c = ch[0]
+            for pas in range(4):
+                for layer in range(60):
+                    q, k, v = pool[(c + 4 * layer + pas) % RESET_EVERY]
+                    if pas == 0:
+                        big.write_attend(layer, k, v, pos_pool[c % RESET_EVERY], q, pos_pool[c % RESET_EVERY], out)
+                    else:
+                        big.attend(layer, q, pos_pool[c % RESET_EVERY], out)
+            ch[0] += 1
+        chunk60()
+        comp["per_chunk_ms"] = timed(chunk60, 3, stream) + comp["rotate_60layer_us"] / 1e3 / RESET_EVERY
         del big
+        torch.cuda.synchronize()
+        # stress shape: 48 heads x 128 (the full width on one GPU), 11,576
+        # slots filled by 16 writes of 757 tokens, one attention call of 757
+        # queries over all of it (timing only: seeded N(0,1) device tensors)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(4)
+        HS, NS = 48, 11576
+        st = rkv.RingCache(1, NS, HS, D, CHUNK, prec, device=dev)
+        ks = torch.randn(CHUNK, HS, D, generator=gen, device=dev).to(torch.bfloat16)
+        vs = torch.randn(CHUNK, HS, D, generator=gen, device=dev).to(torch.bfloat16)
+        qs = torch.randn(CHUNK, HS, D, generator=gen, device=dev).to(torch.bfloat16)
+        for c in range(16):
+            st.write(0, ks, vs, pos_base + CHUNK * c)
+        outs = torch.empty(CHUNK, HS, D, dtype=torch.bfloat16, device=dev)
+        qpos = pos_base + CHUNK * 15
+        st.attend(0, qs, qpos, outs)
+        comp["stress_attend_us"] = 1e3 * timed(lambda: st.attend(0, qs, qpos, outs), 20, stream)
+        comp["stress_attend_TFLOPs"] = STRESS_FLOP / comp["stress_attend_us"] / 1e6
+        assert torch.isfinite(outs.float()).all()
+        del st, ks, vs, qs, outs
         torch.cuda.synchronize()
         peaks = measured_peaks(stream)
 
@@ -371,6 +410,14 @@ def main():
                                "unit": "GB/s", "frac": round(comp["rotate_60layer_GBps"] / PEAK_HBM_GBPS, 4),
                                "bytes": 60 * ROTATE_BYTES},
         }
+        if "stress_attend_TFLOPs" in comp:
+            a = comp["stress_attend_TFLOPs"]
+            res["roofline_stress"] = {"workload": "attend_757x11576_h48", "bound": "mfma", "achieved": round(a, 2),
+                                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(a / PEAK_FP8_TFLOPS, 4),
+                                      "per_launch_flop": STRESS_FLOP,
+                                      "per_launch_us": round(comp["stress_attend_us"], 3)}
+            if peaks:
+                res["roofline_stress"]["frac_of_measured_peak"] = round(a / peaks["fp8_mfma_TFLOPs"], 4)
         if peaks:
             for part in res["roofline_hbm"].values():
                 part["frac_of_measured_peak"] = round(part["achieved"] / peaks["hbm_stream_GBps"], 4)

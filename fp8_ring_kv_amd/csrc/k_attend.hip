@@ -958,16 +958,20 @@ static hipError_t launch_attend_main(const Geom& g, const AttnWs& ws, int layer,
   A.q = (const uint4*)q;
   A.q_pos = q_pos;
   A.out = (uint16_t*)out;
-  // With at most one workgroup slot per unit, the grid is a multiple of the
-  // unit count (preferably also of the 8 XCDs), so that every workgroup's
-  // range lies inside one unit: one segment per workgroup, equal splits.
+  // With at least one workgroup slot per unit, the grid is a multiple of the
+  // unit count (preferably also of the 8 XCDs) that fills at least 7/8 of the
+  // slots, so that every workgroup's range lies inside one unit: one segment
+  // per workgroup, equal splits.  Without such a multiple (e.g. 288 units for
+  // 512 slots) the full grid is used and ranges cross units.
   int G = ws.grid;
   const int U = nqg * g.n_heads;
   if (U <= ws.grid) {
-    int k = ws.grid / U;
-    for (int kk = k; kk >= 1 && U * kk * 8 >= ws.grid * 7; --kk)
-      if (U * kk % 8 == 0) { k = kk; break; }
-    G = U * k;
+    int best = 0;
+    for (int kk = ws.grid / U; kk >= 1 && U * kk * 8 >= ws.grid * 7; --kk) {
+      if (best == 0) best = U * kk;
+      if (U * kk % 8 == 0) { best = U * kk; break; }
+    }
+    if (best > 0) G = best;
   }
   const dim3 grid(G);
   if (D == 128) {
