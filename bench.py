@@ -34,6 +34,8 @@ sys.path.insert(0, ROOT)
 H, D, N, CHUNK, RESET_EVERY = 12, 128, 5788, 757, 42
 ATTN_FLOP = 4.0 * CHUNK * N * H * D  # QK^T and PV, 2 flops per multiply-add
 STRESS_FLOP = 4.0 * CHUNK * 11576 * 48 * D  # the stress shape: 48 heads, 11,576 slots
+STRESS_WRITE_BYTES = (6 * 48 * D + 8 * 48 + 4) * CHUNK  # one 757-token write at 48 heads
+FULL_WRITE_BYTES = (6 * H * D + 8 * H + 4) * N  # one write of 5,788 tokens at 12 heads
 WRITE_BYTES = (6 * H * D + 8 * H + 4) * CHUNK  # bf16 K,V in; e4m3 K,V + 2 scales + pos out
 ROTATE_BYTES = (2 * H * D + 8 * H + 8) * N  # codes r/w, scale r/w, position r/w
 PEAK_FP8_TFLOPS = 5000.0
@@ -360,6 +362,13 @@ def main():
         qs = torch.randn(CHUNK, HS, D, generator=gen, device=dev).to(torch.bfloat16)
         for c in range(16):
             st.write(0, ks, vs, pos_base + CHUNK * c)
+        wc = [16]
+
+        def wst():
+            st.write(0, ks, vs, pos_base + CHUNK * wc[0])
+            wc[0] += 1
+        comp["stress_write_us"] = 1e3 * timed(wst, 50, stream)
+        comp["stress_write_GBps"] = STRESS_WRITE_BYTES / comp["stress_write_us"] / 1e3
         outs = torch.empty(CHUNK, HS, D, dtype=torch.bfloat16, device=dev)
         qpos = pos_base + CHUNK * 15
         st.attend(0, qs, qpos, outs)
@@ -367,6 +376,16 @@ def main():
         comp["stress_attend_TFLOPs"] = STRESS_FLOP / comp["stress_attend_us"] / 1e6
         assert torch.isfinite(outs.float()).all()
         del st, ks, vs, qs, outs
+        # one write of a whole ring's worth of tokens (5,788 x 12 heads, 54 MB
+        # moved): the write kernel with enough work to approach bandwidth
+        fr = rkv.RingCache(1, N, H, D, CHUNK, prec, device=dev)
+        kf = torch.randn(N, H, D, generator=gen, device=dev).to(torch.bfloat16)
+        vf = torch.randn(N, H, D, generator=gen, device=dev).to(torch.bfloat16)
+        pf = torch.arange(N, dtype=torch.int32, device=dev)
+        fr.write(0, kf, vf, pf)
+        comp["write_full_ring_us"] = 1e3 * timed(lambda: fr.write(0, kf, vf, pf), 50, stream)
+        comp["write_full_ring_GBps"] = FULL_WRITE_BYTES / comp["write_full_ring_us"] / 1e3
+        del fr, kf, vf, pf
         torch.cuda.synchronize()
         peaks = measured_peaks(stream)
 
@@ -410,6 +429,11 @@ def main():
                                "unit": "GB/s", "frac": round(comp["rotate_60layer_GBps"] / PEAK_HBM_GBPS, 4),
                                "bytes": 60 * ROTATE_BYTES},
         }
+        for key, nbytes in [("stress_write", STRESS_WRITE_BYTES), ("write_full_ring", FULL_WRITE_BYTES)]:
+            if key + "_GBps" in comp:
+                a = comp[key + "_GBps"]
+                res["roofline_hbm"][key] = {"achieved": round(a, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                            "frac": round(a / PEAK_HBM_GBPS, 4), "bytes": nbytes}
         if "stress_attend_TFLOPs" in comp:
             a = comp["stress_attend_TFLOPs"]
             res["roofline_stress"] = {"workload": "attend_757x11576_h48", "bound": "mfma", "achieved": round(a, 2),

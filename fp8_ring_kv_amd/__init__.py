@@ -299,6 +299,13 @@ class RingCache:
         lay = self.layout(layer)
         return self._view(lay.state, 16, torch.int32)
 
+    def write_counters(self, layer: int) -> torch.Tensor:
+        """The write kernel's ticket counters (top, then one per sub-counter line),
+        int32 on device; zero between calls."""
+        lay = self.layout(layer)
+        region = self._view(lay.state, 4 * 64 * 9, torch.int32)
+        return torch.cat([region[2:4], region[64::64]])
+
     def vmax(self, layer: int) -> torch.Tensor:
         """[H] float32: largest value scale written to each head since the reset."""
         lay = self.layout(layer)

@@ -56,7 +56,8 @@ __global__ void reset_kernel(Geom g, int layer_lo) {
   const LayerPtrs L = layer_ptrs(g, layer_lo + (int)blockIdx.y);
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < g.n_pad) L.slot_pos[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x < kStateInts) L.state[threadIdx.x] = 0;
+  if (blockIdx.x == 0)
+    for (int j = (int)threadIdx.x; j < kStateRegionInts; j += (int)blockDim.x) L.state[j] = 0;
   if (blockIdx.x == 0)
     for (int j = (int)threadIdx.x; j < g.n_heads * kSub; j += (int)blockDim.x) L.vmax[j] = 0u;
 }

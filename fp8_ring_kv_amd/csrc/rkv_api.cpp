@@ -95,7 +95,7 @@ Plan make_plan(const rkv_params* p) {
   g.off_slot_pos = o;
   o = align_up(o + NP * 4, kAlign);
   g.off_state = o;
-  o = align_up(o + rkv::kStateInts * 4, kAlign);
+  o = align_up(o + rkv::kStateRegionInts * 4, kAlign);
   g.off_vmax = o;
   o = align_up(o + H * rkv::kSub * 4, kAlign);
   g.layer_bytes = o;

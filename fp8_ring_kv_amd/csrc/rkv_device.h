@@ -15,7 +15,15 @@ constexpr int kMaxHalfDim = 64;  // D/2 for the largest supported head_dim (128)
 // Per-head value-scale maxima are spread over kSub slots so that no single
 // address takes more than a fraction of one launch's atomics.
 constexpr int kSub = 8;
-constexpr int kStateInts = 4;  // head, n_valid, write ticket counter, 0
+constexpr int kStateInts = 4;  // head, n_valid, top ticket counter of the write, 0
+// A large write counts its tickets on kTicketSub sub-counters, each on its
+// own 256-byte line kTicketStride ints past the previous one (sub-counter j
+// at state[kTicketStride * (1 + j)]): atomics on one address serialize, so
+// one counter for every workgroup of a large write cost ~15 ns per workgroup.
+constexpr int kTicketSub = 8;
+constexpr int kTicketStride = 64;
+constexpr int kTicketSplitMin = 512;  // workgroups above which the tickets use the sub-counters
+constexpr int kStateRegionInts = kTicketStride * (1 + kTicketSub);
 
 // Byte offsets of one layer's arrays (relative to the layer's start) and the
 // sizes every kernel needs.  Passed by value as a kernel argument.
@@ -35,7 +43,7 @@ struct LayerPtrs {
   float* scale_k;
   float* scale_v;
   int32_t* slot_pos;
-  int32_t* state;  // {head, n_valid, write ticket counter, 0}
+  int32_t* state;  // {head, n_valid, top ticket counter, 0}, sub-counters at kTicketStride * (1 + j)
   uint32_t* vmax;  // [H][kSub] largest value scale written since the reset (fp32
                    // bits); the head's bound is the max over its kSub entries
 };

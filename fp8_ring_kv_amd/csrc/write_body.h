@@ -60,12 +60,17 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
     }
     p = pos[i];
   }
-  // Ticket for the device-side write position, one per workgroup on one
-  // counter, taken once head and n_valid are read (the increment depends on
-  // the loaded head; it is always 1).  Whoever takes the last ticket knows
-  // that every workgroup has read the position and may advance it.  No
-  // workgroup reads what another writes: relaxed device-scope atomics
-  // suffice; the next kernel on the stream sees the new state.
+  // Ticket for the device-side write position, taken once head and n_valid
+  // are read (the increment depends on the loaded head; it is always 1).
+  // Whoever takes the last ticket knows that every workgroup has read the
+  // position and may advance it.  Up to kTicketSplitMin workgroups count on
+  // the top counter alone.  Larger grids count workgroup w on sub-counter
+  // w mod kTicketSub and the last of each sub-group on the top counter:
+  // atomics on one address serialize (~15 ns each), which cost a
+  // 2,184-workgroup write 13 us, while the second level adds one atomic
+  // round trip at the end (0.4 us on a 294-workgroup write).  No workgroup
+  // reads what another writes: relaxed device-scope atomics suffice; the
+  // next kernel on the stream sees the new state.
   // The ticket goes out once every load of this workgroup has returned (the
   // frequency table included): vector memory operations complete in order, so
   // a wait for a load issued after the ticket, or one the compiler cannot
@@ -80,10 +85,13 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
     asm volatile("" ::"v"(kw[hh].x), "v"(kw[hh].y), "v"(kw[hh].z), "v"(kw[hh].w), "v"(vw[hh].x), "v"(vw[hh].y),
                  "v"(vw[hh].z), "v"(vw[hh].w));
   asm volatile("" ::"v"(p), "v"(tw[0]), "v"(tw[1]), "v"(tw[2]), "v"(tw[3]) : "memory");
+  const int wgi = by * gx + bx, nwg = gx * gy;
+  const bool two_level = nwg > kTicketSplitMin;
+  const int sub = wgi % kTicketSub;
+  int* const counter = two_level ? L.state + kTicketStride * (1 + sub) : L.state + 2;
   int ticket = -1;
   if (threadIdx.x == 0)
-    ticket = __hip_atomic_fetch_add(&L.state[2], head < 0x7FFFFFFF ? 1 : 2, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
+    ticket = __hip_atomic_fetch_add(counter, head < 0x7FFFFFFF ? 1 : 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // angles for every lane (the table index is always in range; inactive
   // lanes rotate zeros)
   float cs[4], sn[4];
@@ -185,12 +193,23 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, vmx[threadIdx.x][e]);
     if (mx > 0.f) atomicMax(&L.vmax[(h0 + threadIdx.x) * kSub + bx % kSub], __float_as_uint(mx));
   }
-  // The workgroup that took the last ticket advances the device-side write
-  // position (every workgroup had read it before taking its ticket).
-  if (threadIdx.x == 0 && ticket == gx * gy - 1) {
-    __hip_atomic_store(&L.state[2], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    L.state[0] = (int)(((long long)head + n) % N);
-    L.state[1] = nvalid + n < N ? nvalid + n : N;
+  // Two levels: the last workgroup of a sub-group clears its sub-counter and
+  // takes a top ticket.  The one that takes the last top ticket clears the
+  // top counter and advances the device-side write position (every
+  // workgroup had read it before taking its ticket).
+  if (threadIdx.x == 0) {
+    bool last = false;
+    if (!two_level) {
+      last = ticket == nwg - 1;
+    } else if (ticket == (nwg - sub + kTicketSub - 1) / kTicketSub - 1) {
+      __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = __hip_atomic_fetch_add(&L.state[2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == kTicketSub - 1;
+    }
+    if (last) {
+      __hip_atomic_store(&L.state[2], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      L.state[0] = (int)(((long long)head + n) % N);
+      L.state[1] = nvalid + n < N ? nvalid + n : N;
+    }
   }
 }
 

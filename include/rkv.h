@@ -89,11 +89,13 @@ typedef struct {
  *   scale_k  f32 [H][N_pad]           per-(slot, head) key scale
  *   scale_v  f32 [H][N_pad]           per-(slot, head) value scale
  *   slot_pos i32 [N_pad]              position each slot was written with
- *   state    i32 [4]                  {head, n_valid, ...}: the next write
+ *   state    i32 [576]                {head, n_valid, ...}: the next write
  *                                      slot and the number of valid slots
  *                                      (the cyclic range [head-n_valid,
- *                                      head)); the other two are a counter
- *                                      internal to the write kernel and 0.
+ *                                      head)); the rest are ticket counters
+ *                                      internal to the write kernel (a top
+ *                                      counter at [2], 8 sub-counters at
+ *                                      [64 (1 + j)]), zero between calls.
  *   vmax     f32 [H][8]               per head, the largest value scale
  *                                      written since the last reset (an upper
  *                                      bound of every cached value scale) is

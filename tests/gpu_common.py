@@ -77,8 +77,8 @@ def assert_cache_matches(cache, layer, st, slots=None, check_v=True, pre=None):
     (head, nv), sp, ck, cv, sk, sv = readback(cache, layer)
     assert (head, nv) == (st.head, st.n_valid), ((head, nv), (st.head, st.n_valid))
     # the write kernel's internal counters are back at zero after every call
-    counters = cache.state(layer).cpu().numpy()[2:12]
-    assert not counters.any(), counters
+    counters = cache.write_counters(layer).cpu().numpy()
+    assert len(counters) == 10 and not counters.any(), counters
     # the per-head value-scale bound equals the oracle's (fp32 values)
     vmax = cache.vmax(layer).cpu().numpy().astype(np.float64)
     assert np.array_equal(vmax, st.vmax), (vmax, st.vmax)

@@ -97,6 +97,25 @@ def test_value_codes_and_scales_bit_exact(margin):
     assert np.array_equal(got[~zero], want[~zero]) and np.all((got[zero] & 0x7F) == 0)
 
 
+def test_large_writes_take_two_level_tickets():
+    """A 2,000-token write at 12 heads is 762 workgroups, above the 512 that
+    count their tickets on one counter: the ring position must still advance
+    exactly once per call, with every counter back at zero, before and after
+    a small write that uses the single counter."""
+    cfg = Config("bigwrite", n_heads=12, head_dim=128, n_slots=2100, chunk=0, seed=12,
+                 outliers=OutlierSpec(0.02, 8.0))
+    cache, st = new_pair(cfg)
+    s = Stream(cfg)
+    p0 = 0
+    for n in (2000, 300, 2000):
+        _, k, v = s.chunk(n)
+        pos = positions(p0, n)
+        cache.write(0, to_dev(k), to_dev(v), pos_dev(pos))
+        oring.write(st, k.f64, v.f64, pos)
+        p0 += n
+        assert_cache_matches(cache, 0, st)
+
+
 @pytest.mark.parametrize("head_dim", [64, 128])
 def test_wrapping_writes_of_varied_sizes(head_dim):
     """Random write sizes (1 .. N, including a full-ring write) wrap the ring many times."""
