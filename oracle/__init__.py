@@ -25,9 +25,13 @@ Diffusion Transformer for Real-Time Conversation" (arXiv:2611.05642):
 Pins: every function is checked in ``tests/test_oracle_*.py`` and
 ``tests/test_codec.py`` against something other than itself (torch's CPU
 float8 cast, closed forms, brute-force loops, torch's float64 attention, the
-rotation identity).  ``attend.attend_emul`` is pinned only by special cases
-and error bounds relative to ``attend_method``; its rounding of the
-probabilities to FP8 has no external reference ("parity partially pinned").
+rotation identity).  ``attend.attend_emul`` (the device kernel's declared
+numerics, not a rule of the paper) is pinned by exact facts: its output
+scales by exactly 2^k when every value scale does; with every scaled
+probability an e4m3 value (one valid slot, or identical keys with value
+scales at power-of-two fractions of vmax) it equals the closed form; its
+two-term probability split has closed forms and an error bound; and its
+e4m3 rounding is the codec pinned against torch's cast.
 """
 
 from . import e4m3, rope, ring, attend, bf16  # noqa: F401

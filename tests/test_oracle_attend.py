@@ -288,3 +288,46 @@ def test_declared_numerics_meet_contract_on_outlier_cache():
     sig = np.maximum(1.0, attend.sigma_v(st))[None]
     e = np.abs(em - ex) / sig
     assert e.max() < 2e-2 and e.mean() < 2e-3
+
+
+def test_emul_scales_exactly_with_power_of_two_value_scales():
+    """Multiplying every value scale (and so vmax) by 2^k leaves each P s_v c
+    unchanged (c divides by vmax) and the output scales by exactly 2^k: a
+    value scale applied twice, or c missing from the normalization, breaks it."""
+    st, chunks = tiny_session()
+    q, _, _, pos = chunks[5]
+    base = attend.attend_emul(st, q.f64, pos)
+    for k in (-3, 5):
+        s2 = st.copy()
+        s2.scale_v = st.scale_v * 2.0 ** k
+        s2.vmax = st.vmax * 2.0 ** k
+        got = attend.attend_emul(s2, q.f64, pos)
+        assert np.array_equal(got, base * 2.0 ** k), k
+
+
+def test_emul_exact_when_scaled_probabilities_are_representable():
+    """Identical keys make every probability 1; value scales at power-of-two
+    fractions of vmax make each P s_v c = 112 * 2^-m an e4m3 value, so both
+    terms are exact and the output is the mean of the dequantized values
+    (vmax a power of two, so that c = 112 / vmax is exact in fp32)."""
+    rng = np.random.default_rng(21)
+    n, d = 24, 32
+    st = ring.RingState(n, 1, d)
+    k = np.repeat(rng.standard_normal((1, 1, d)), n, axis=0)
+    v = rng.standard_normal((n, 1, d))
+    ring.write(st, k, v, np.zeros(n, dtype=np.int64))
+    big = 4.0
+    m = rng.integers(0, 9, size=n)
+    st.scale_v[0, :] = big * 2.0 ** (-m)
+    st.vmax[0] = big
+    q = rng.standard_normal((5, 1, d))
+    mean_v = (e4m3.decode(st.codes_v[0]) * st.scale_v[0][:, None]).mean(axis=0)
+    for terms in (1, 2):
+        out = attend.attend_emul(st, q, np.arange(5), p_terms=terms)
+        assert np.max(np.abs(out[:, 0, :] - mean_v[None])) <= 1e-14 * np.max(np.abs(mean_v)), terms
+    # a value scale above vmax would push P s_v c past 112 (the headroom) but
+    # still inside e4m3 for a factor of 4: the same closed form holds
+    st.scale_v[0, 0] = big * 4.0
+    mean_v = (e4m3.decode(st.codes_v[0]) * st.scale_v[0][:, None]).mean(axis=0)
+    out = attend.attend_emul(st, q, np.arange(5))
+    assert np.max(np.abs(out[:, 0, :] - mean_v[None])) <= 1e-14 * np.max(np.abs(mean_v))
