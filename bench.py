@@ -10,13 +10,15 @@ position reset: a delta rotation of every cached key by -42 * 757.  The
 cache starts full with its ring head at slot 3,100 (8,888 tokens written).
 
 Prints one JSON line.  `value` is microseconds per step (= per attention call
-with its cache work, resets amortized), launched eagerly on one stream.  The
-same steps captured once as HIP graphs (the device-side write position makes
-every call capturable) and replayed are reported as
-`components.graph_us_per_step`.  Per-operation times come from separate
-HIP-event-timed loops on the launch stream; `roofline` is the attention call
-(the dominant cost) against the dense FP8 matrix peak.  `cpu_baseline` times
-the NumPy float64 oracle on a bounded sample.
+with its cache work, resets amortized).  The steps run first with eager
+launches (`components.eager_us_per_step`); when --steps is a whole number of
+42-step reset periods (the default 84), the same steps are then captured as
+one HIP graph per period (the device-side write position makes every call
+capturable) and replayed, and `value` is the replayed time (`launch` says
+which).  Per-operation times come from separate HIP-event-timed loops on the
+launch stream; `roofline` is the attention call (the dominant cost) against
+the dense FP8 matrix peak.  `cpu_baseline` times the NumPy float64 oracle on
+a bounded sample.
 """
 from __future__ import annotations
 
@@ -55,7 +57,8 @@ def parse():
     ap.add_argument("--reps", type=int, default=200, help="launches per component loop")
     ap.add_argument("--workgroups", type=int, default=0,
                     help="persistent workgroups per attention call (0 = one per compute unit)")
-    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="report the eager launches as value (no HIP-graph capture and replay)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the steps, run one plain copy kernel over this many MiB "
                          "(fp32 negation, read + write): the reference for HBM byte counters")
@@ -181,41 +184,25 @@ def measured_peaks(stream):
                       "rkv_probe_stream (in-place read-modify-write of 1 GiB, 2 GiB moved)"}
 
 
-def graph_step_ms(args, cache, pool, pos_pool, out, stream):
-    """The bench steps captured once as HIP graphs (one per step of the reset
-    period, the rotation in the first) and replayed, continuing the eager step
-    sequence: the device-side write position makes every call capturable.
-    Average milliseconds per replayed step."""
+def capture_period(cache, pool, pos_pool, out):
+    """The 42 steps of a reset period (the rotation first) captured as ONE HIP
+    graph: the same kernels as the eager steps, one graph launch per period.
+    The device-side write position is what makes the calls capturable."""
     import torch
-    graphs = []
+    stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
-        for j in range(RESET_EVERY):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=side):
+        with torch.cuda.graph(g, stream=side):
+            for j in range(RESET_EVERY):
                 if j == 0:
                     cache.rotate(0, -RESET_EVERY * CHUNK)
                 q, k, v = pool[j]
                 cache.write_attend(0, k, v, pos_pool[j], q, pos_pool[j], out)
-            graphs.append(g)
     stream.wait_stream(side)
     torch.cuda.synchronize()
-    first = args.warmup + args.steps
-    for i in range(args.warmup):
-        graphs[(first + i) % RESET_EVERY].replay()
-    first += args.warmup
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for i in range(args.steps):
-        graphs[(first + i) % RESET_EVERY].replay()
-    b.record(stream)
-    b.synchronize()
-    torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all()
-    return a.elapsed_time(b) / args.steps
+    return g
 
 
 def main():
@@ -277,8 +264,30 @@ def main():
     b.synchronize()
     torch.cuda.synchronize()
     host_s = time.perf_counter() - t_host0
-    ms_per_step = a.elapsed_time(b) / args.steps
+    eager_ms = a.elapsed_time(b) / args.steps
     assert torch.isfinite(out.float()).all()
+    ms_per_step, launch = eager_ms, "eager (one HIP launch per kernel)"
+    idx = args.warmup + args.steps
+    if not args.no_graph and args.steps % RESET_EVERY == 0:
+        # The same steps as captured reset periods: continue eagerly to a period
+        # boundary (untimed), capture one period, replay it once (untimed
+        # warm-up), then time exactly args.steps steps of replays.
+        while idx % RESET_EVERY:
+            step_fast(idx)
+            idx += 1
+        g = capture_period(cache, pool, pos_pool, out)
+        g.replay()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(args.steps // RESET_EVERY):
+            g.replay()
+        b.record(stream)
+        b.synchronize()
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all()
+        ms_per_step = a.elapsed_time(b) / args.steps
+        launch = "hip_graph (one graph per 42-step reset period, replayed)"
+        del g
 
     if args.copy_mib:
         # reference kernel for the byte counters: reads and writes copy_mib MiB once
@@ -290,8 +299,7 @@ def main():
 
     comp = {}
     peaks = None
-    if not args.no_graph:
-        comp["graph_us_per_step"] = 1e3 * graph_step_ms(args, cache, pool, pos_pool, out, stream)
+    comp["eager_us_per_step"] = 1e3 * eager_ms
     if not args.no_components:
         r = args.reps
         q0, k0, v0 = pool[0]
@@ -406,6 +414,7 @@ def main():
                    "new_tokens": CHUNK, "queries": CHUNK, "reset_every": RESET_EVERY,
                    "ring_head_start": 3100, "precision": args.precision,
                    "outliers": "2% of channels x8"},
+        "launch": launch,
         "host_wall_s": round(host_s, 4),
     }
     if comp:
