@@ -395,6 +395,19 @@ def main():
         comp["write_full_ring_GBps"] = FULL_WRITE_BYTES / comp["write_full_ring_us"] / 1e3
         del fr, kf, vf, pf
         torch.cuda.synchronize()
+        # fused pre-attention RMS norm of Q and K (the same calls with the norm on)
+        q0, k0, v0 = pool[0]
+        wa = lambda: cache.write_attend(0, k0, v0, pos_pool[0], q0, pos_pool[0], out)
+        comp["write_attend_us"] = 1e3 * timed(wa, r, stream)
+        gen_w = torch.Generator(device=dev)
+        gen_w.manual_seed(5)
+        wq = (1 + 0.25 * torch.randn(D, generator=gen_w, device=dev)).to(torch.bfloat16)
+        wk = (1 + 0.25 * torch.randn(D, generator=gen_w, device=dev)).to(torch.bfloat16)
+        cache.set_qk_norm(0, wq, wk, 1e-6)
+        comp["write_qk_norm_us"] = 1e3 * timed(lambda: cache.write(0, k0, v0, pos_pool[0]), r, stream)
+        comp["write_attend_qk_norm_us"] = 1e3 * timed(wa, r, stream)
+        cache.set_qk_norm(0, None, None)
+        torch.cuda.synchronize()
         peaks = measured_peaks(stream)
 
     res = {

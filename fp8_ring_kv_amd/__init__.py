@@ -23,7 +23,7 @@ __all__ = [
     "rkv_params", "rkv_layout", "RkvError", "lib", "lib_path",
     "ring_cache_bytes", "ring_cache_create", "ring_cache_destroy", "ring_cache_reset",
     "ring_cache_layout", "cache_write_rope_fp8", "cache_delta_rotate", "cache_attend",
-    "cache_write_attend",
+    "cache_write_attend", "ring_cache_set_qk_norm",
     "rkv_last_error", "rkv_probe_fp8_mfma", "rkv_probe_stream", "RingCache",
 ]
 
@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
     L.cache_write_attend.restype = ctypes.c_int
     L.rkv_last_error.argtypes = []
     L.rkv_last_error.restype = ctypes.c_char_p
+    L.ring_cache_set_qk_norm.argtypes = [VP, I32, VP, VP, ctypes.c_float, VP]
+    L.ring_cache_set_qk_norm.restype = ctypes.c_int
     L.rkv_probe_fp8_mfma.argtypes = [I32, I32, VP, VP]
     L.rkv_probe_fp8_mfma.restype = ctypes.c_int
     L.rkv_probe_stream.argtypes = [VP, SZ, VP]
@@ -179,6 +181,13 @@ def cache_write_attend(handle: int, layer: int, k: int, v: int, pos: int, n: int
         raise RkvError(rc, "cache_write_attend")
 
 
+def ring_cache_set_qk_norm(handle: int, layer: int, wq: int, wk: int, eps: float, stream: int) -> None:
+    rc = lib().ring_cache_set_qk_norm(ctypes.c_void_p(handle), layer, ctypes.c_void_p(wq), ctypes.c_void_p(wk),
+                                      eps, ctypes.c_void_p(stream))
+    if rc != RKV_OK:
+        raise RkvError(rc, "ring_cache_set_qk_norm")
+
+
 # ---- measurement aids (include/rkv_probe.h) ----------------------------------
 
 def rkv_probe_fp8_mfma(workgroups: int, iters: int, sink: int, stream: int) -> None:
@@ -249,6 +258,18 @@ class RingCache:
         _check(pos, torch.int32, (n,), "pos")
         cache_write_rope_fp8(self.handle, layer, k.data_ptr(), v.data_ptr(), pos.data_ptr(), n,
                              _stream_handle(stream))
+
+    def set_qk_norm(self, layer: int, wq: torch.Tensor | None, wk: torch.Tensor | None, eps: float = 1e-6,
+                    stream=None):
+        """Fused Q/K RMS norm for `layer` (-1: all) with bf16 [head_dim] weights; None, None turns it off.
+        The weight tensors are kept alive here until the next call (the copy is asynchronous)."""
+        if wq is None and wk is None:
+            ring_cache_set_qk_norm(self.handle, layer, 0, 0, eps, _stream_handle(stream))
+            return
+        for t, nm in ((wq, "wq"), (wk, "wk")):
+            _check(t, torch.bfloat16, (self.head_dim,), nm)
+        self._norm_refs = (wq, wk)
+        ring_cache_set_qk_norm(self.handle, layer, wq.data_ptr(), wk.data_ptr(), eps, _stream_handle(stream))
 
     def rotate(self, layer: int, delta: int, stream=None):
         cache_delta_rotate(self.handle, layer, int(delta), _stream_handle(stream))

@@ -414,6 +414,8 @@ struct QPrepArgs {
   const uint4* q;  // bf16 [n_q][H][D]
   const int32_t* q_pos;
   float qscale;  // softmax scale in log2 units, log2(e) / sqrt(D), rounded once to float
+  const uint16_t* wq;  // query RMS-norm weights (bf16 [D]) of the fused pre-attention norm, null when off
+  float eps;           // its epsilon
 };
 
 // Body of one 256-thread workgroup number `block` of the preparation.
@@ -437,18 +439,39 @@ __device__ inline void q_prep_body(const QPrepArgs& A, int block) {
   const uint4* qp = A.q + ((size_t)qr * H + h) * (D / 8) + part * (EPT / 8);
   const int32_t p = A.q_pos[qr];
   const double* turns = omega_turns(A.g) + part * (EPT / 2);
-  float y[EPT];
-  float am = 0.f;
+  float xs[EPT];
 #pragma unroll
   for (int c = 0; c < EPT / 8; ++c) {
     const uint4 w = qp[c];
     const float xv[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                          bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
 #pragma unroll
+    for (int e = 0; e < 8; ++e) xs[8 * c + e] = active ? xv[e] : 0.f;
+  }
+  if (A.wq != nullptr) {  // fused RMS norm of the query row, before RoPE
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) ss = fmaf(xs[e], xs[e], ss);
+    const float rn = rms_factor<TPR>(ss, 1.f / D, A.eps);
+    const uint4* wp = reinterpret_cast<const uint4*>(A.wq) + part * (EPT / 8);
+#pragma unroll
+    for (int c = 0; c < EPT / 8; ++c) {
+      const uint4 w = wp[c];
+      const float wv[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                           bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[8 * c + e] = xs[8 * c + e] * rn * wv[e];
+    }
+  }
+  float y[EPT];
+  float am = 0.f;
+#pragma unroll
+  for (int c = 0; c < EPT / 8; ++c) {
+#pragma unroll
     for (int m = 0; m < 4; ++m) {
       float cs, sn;
       rope_cs(p, turns[4 * c + m], cs, sn);
-      const float x0 = active ? xv[2 * m] : 0.f, x1 = active ? xv[2 * m + 1] : 0.f;
+      const float x0 = xs[8 * c + 2 * m], x1 = xs[8 * c + 2 * m + 1];
       y[8 * c + 2 * m] = (x0 * cs - x1 * sn) * A.qscale;
       y[8 * c + 2 * m + 1] = (x0 * sn + x1 * cs) * A.qscale;
       am = fmaxf(am, fmaxf(fabsf(y[8 * c + 2 * m]), fabsf(y[8 * c + 2 * m + 1])));
@@ -505,13 +528,15 @@ struct WritePrepArgs {
   const int32_t* pos;
   int n;
   int wgx, wgy;  // the write's grid
+  const uint16_t* wk;  // key RMS-norm weights, null when off (epsilon in P.eps)
 };
 
 template <int HG, int TERMS>
 __global__ __launch_bounds__(256) void write_prep_kernel(WritePrepArgs W) {
   const int b = (int)blockIdx.x, nw = W.wgx * W.wgy;
   if (b < nw)
-    write_rope_fp8_body<128, HG>(W.P.g, W.layer, W.k, W.v, W.pos, W.n, b % W.wgx, b / W.wgx, W.wgx, W.wgy);
+    write_rope_fp8_body<128, HG>(W.P.g, W.layer, W.k, W.v, W.pos, W.n, W.wk, W.P.eps, b % W.wgx, b / W.wgx, W.wgx,
+                                 W.wgy);
   else
     q_prep_body<128, TERMS>(W.P, b - nw);
 }
@@ -926,8 +951,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
   }
 }
 
-static QPrepArgs make_prep_args(const Geom& g, const AttnWs& ws, const void* q, const int32_t* q_pos, int n_q) {
+static QPrepArgs make_prep_args(const Geom& g, const AttnWs& ws, const void* q, const int32_t* q_pos, int n_q,
+                                const uint16_t* wq, float eps) {
   QPrepArgs P;
+  P.wq = wq;
+  P.eps = eps;
   P.g = g;
   P.ws = ws;
   P.n_q = n_q;
@@ -985,8 +1013,9 @@ static hipError_t launch_attend_main(const Geom& g, const AttnWs& ws, int layer,
 }
 
 hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void* q,
-                         const int32_t* q_pos, int n_q, void* out, hipStream_t s) {
-  const QPrepArgs P = make_prep_args(g, ws, q, q_pos, n_q);
+                         const int32_t* q_pos, int n_q, void* out, const uint16_t* wq, float eps,
+                         hipStream_t s) {
+  const QPrepArgs P = make_prep_args(g, ws, q, q_pos, n_q, wq, eps);
   const dim3 pgrid(prep_blocks(P));
   if (g.head_dim == 128) {
     if (ws.terms == 2) hipLaunchKernelGGL((q_prep_kernel<128, 2>), pgrid, dim3(256), 0, s, P);
@@ -1008,14 +1037,15 @@ static void launch_write_prep_t(const WritePrepArgs& W, int blocks, int terms, h
 
 hipError_t launch_write_attend(const Geom& g, const AttnWs& ws, int layer, const void* k, const void* v,
                                const int32_t* pos, int n, const void* q, const int32_t* q_pos, int n_q,
-                               void* out, hipStream_t s) {
+                               void* out, const uint16_t* wq, const uint16_t* wk, float eps, hipStream_t s) {
   if (g.head_dim != 128) {  // 128-thread write workgroups: two launches, then the attention
-    hipError_t e = launch_write(g, layer, k, v, pos, n, s);
+    hipError_t e = launch_write(g, layer, k, v, pos, n, wk, eps, s);
     if (e != hipSuccess) return e;
-    return launch_attend(g, ws, layer, q, q_pos, n_q, out, s);
+    return launch_attend(g, ws, layer, q, q_pos, n_q, out, wq, eps, s);
   }
   WritePrepArgs W;
-  W.P = make_prep_args(g, ws, q, q_pos, n_q);
+  W.P = make_prep_args(g, ws, q, q_pos, n_q, wq, eps);
+  W.wk = wk;
   W.layer = layer;
   W.k = (const uint4*)k;
   W.v = (const uint4*)v;

@@ -73,29 +73,29 @@ hipError_t launch_reset(const Geom& g, int layer_lo, int layer_hi, hipStream_t s
 template <int D, int HG>
 __global__ __launch_bounds__(16 * (D / 8)) void write_rope_fp8_kernel(
     Geom g, int layer, const uint4* __restrict__ k, const uint4* __restrict__ v,
-    const int32_t* __restrict__ pos, int n) {
-  write_rope_fp8_body<D, HG>(g, layer, k, v, pos, n, (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x,
+    const int32_t* __restrict__ pos, int n, const uint16_t* wk, float eps) {
+  write_rope_fp8_body<D, HG>(g, layer, k, v, pos, n, wk, eps, (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x,
                              (int)gridDim.y);
 }
 
 template <int D, int HG>
 static void launch_write_t(const Geom& g, int layer, const void* k, const void* v, const int32_t* pos,
-                           int n, int groups, hipStream_t s) {
+                           int n, const uint16_t* wk, float eps, int groups, hipStream_t s) {
   dim3 grid(groups, g.n_heads / HG);
   hipLaunchKernelGGL((write_rope_fp8_kernel<D, HG>), grid, dim3(16 * (D / 8)), 0, s, g, layer,
-                     (const uint4*)k, (const uint4*)v, pos, n);
+                     (const uint4*)k, (const uint4*)v, pos, n, wk, eps);
 }
 
 hipError_t launch_write(const Geom& g, int layer, const void* k, const void* v, const int32_t* pos,
-                        int n, hipStream_t s) {
+                        int n, const uint16_t* wk, float eps, hipStream_t s) {
   int groups, hg;
   write_grid(g, n, &groups, &hg);
   if (g.head_dim == 128) {
-    if (hg == 2) launch_write_t<128, 2>(g, layer, k, v, pos, n, groups, s);
-    else launch_write_t<128, 1>(g, layer, k, v, pos, n, groups, s);
+    if (hg == 2) launch_write_t<128, 2>(g, layer, k, v, pos, n, wk, eps, groups, s);
+    else launch_write_t<128, 1>(g, layer, k, v, pos, n, wk, eps, groups, s);
   } else {
-    if (hg == 2) launch_write_t<64, 2>(g, layer, k, v, pos, n, groups, s);
-    else launch_write_t<64, 1>(g, layer, k, v, pos, n, groups, s);
+    if (hg == 2) launch_write_t<64, 2>(g, layer, k, v, pos, n, wk, eps, groups, s);
+    else launch_write_t<64, 1>(g, layer, k, v, pos, n, wk, eps, groups, s);
   }
   return hipGetLastError();
 }

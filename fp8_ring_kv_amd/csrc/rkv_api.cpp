@@ -8,6 +8,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "rkv_launch.h"
 
@@ -98,6 +99,8 @@ Plan make_plan(const rkv_params* p) {
   o = align_up(o + rkv::kStateRegionInts * 4, kAlign);
   g.off_vmax = o;
   o = align_up(o + H * rkv::kSub * 4, kAlign);
+  g.off_normw = o;
+  o = align_up(o + 2 * D * 2, kAlign);
   g.layer_bytes = o;
 
   size_t w = g.layer0 + (size_t)p->n_layers * g.layer_bytes;
@@ -138,6 +141,14 @@ struct rkv_cache {
   size_t bytes;
   double half_turns[rkv::kMaxHalfDim];  // omega_j / (2 pi)
   double omega[rkv::kMaxHalfDim];
+  std::vector<float> norm_eps;  // per layer: eps of the fused Q/K RMS norm, < 0 when off
+  // the layer's query and key norm weights (bf16 [D] each), null when off
+  const uint16_t* norm_q(int layer) const {
+    return norm_eps[layer] >= 0.f ? rkv::layer_ptrs(g, layer).normw : nullptr;
+  }
+  const uint16_t* norm_k(int layer) const {
+    return norm_eps[layer] >= 0.f ? rkv::layer_ptrs(g, layer).normw + g.head_dim : nullptr;
+  }
 };
 
 extern "C" {
@@ -178,6 +189,7 @@ int ring_cache_create(const rkv_params* p, void* dev_buf, size_t bytes, hipStrea
   c->ws.qcodes = c->g.base + pl.ws_qcodes;
   c->ws.qexp = reinterpret_cast<int32_t*>(c->g.base + pl.ws_qexp);
   c->bytes = pl.total;
+  c->norm_eps.assign(p->n_layers, -1.f);
   const int half = p->head_dim / 2;
   for (int j = 0; j < half; ++j) {
     c->omega[j] = std::pow((double)p->rope_base, -2.0 * j / p->head_dim);
@@ -255,7 +267,7 @@ int cache_write_rope_fp8(rkv_cache* c, int32_t layer, const void* k_bf16, const 
   if (!aligned(pos, 4)) return fail(RKV_EINVAL, "pos must be 4-byte aligned");
   if (n < 1 || n > c->p.n_slots)
     return fail(RKV_EINVAL, "n = " + std::to_string(n) + " outside [1, n_slots]");
-  hipError_t e = rkv::launch_write(c->g, layer, k_bf16, v_bf16, pos, n, stream);
+  hipError_t e = rkv::launch_write(c->g, layer, k_bf16, v_bf16, pos, n, c->norm_k(layer), c->norm_eps[layer], stream);
   if (e != hipSuccess) return hip_fail(e, "write kernel launch");
   return RKV_OK;
 }
@@ -287,7 +299,8 @@ int cache_attend(rkv_cache* c, int32_t layer, const void* q_bf16, const int32_t*
   if (!aligned(q_pos, 4)) return fail(RKV_EINVAL, "q_pos must be 4-byte aligned");
   if (n_q < 1 || n_q > c->p.max_queries)
     return fail(RKV_EINVAL, "n_q = " + std::to_string(n_q) + " outside [1, max_queries]");
-  hipError_t e = rkv::launch_attend(c->g, c->ws, layer, q_bf16, q_pos, n_q, out_bf16, stream);
+  hipError_t e = rkv::launch_attend(c->g, c->ws, layer, q_bf16, q_pos, n_q, out_bf16, c->norm_q(layer),
+                                     c->norm_eps[layer], stream);
   if (e != hipSuccess) return hip_fail(e, "attend kernel launch");
   return RKV_OK;
 }
@@ -308,8 +321,34 @@ int cache_write_attend(rkv_cache* c, int32_t layer, const void* k_bf16, const vo
   if (n_q < 1 || n_q > c->p.max_queries)
     return fail(RKV_EINVAL, "n_q = " + std::to_string(n_q) + " outside [1, max_queries]");
   hipError_t e = rkv::launch_write_attend(c->g, c->ws, layer, k_bf16, v_bf16, pos, n, q_bf16, q_pos, n_q,
-                                          out_bf16, stream);
+                                          out_bf16, c->norm_q(layer), c->norm_k(layer), c->norm_eps[layer],
+                                          stream);
   if (e != hipSuccess) return hip_fail(e, "write/attend kernel launch");
+  return RKV_OK;
+}
+
+int ring_cache_set_qk_norm(rkv_cache* c, int32_t layer, const void* wq_bf16, const void* wk_bf16, float eps,
+                           hipStream_t stream) {
+  if (!c) return fail(RKV_EINVAL, "cache is null");
+  int lo, hi;
+  if (int r = layer_range(c, layer, true, &lo, &hi)) return r;
+  if (!wq_bf16 && !wk_bf16) {
+    for (int l = lo; l < hi; ++l) c->norm_eps[l] = -1.f;
+    g_err.clear();
+    return RKV_OK;
+  }
+  if (!wq_bf16 || !wk_bf16) return fail(RKV_EINVAL, "wq and wk must both be set or both be null");
+  if (!aligned(wq_bf16, 2) || !aligned(wk_bf16, 2)) return fail(RKV_EINVAL, "weights must be 2-byte aligned");
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(RKV_EINVAL, "eps must be finite and > 0");
+  const size_t bytes = (size_t)c->p.head_dim * 2;
+  for (int l = lo; l < hi; ++l) {
+    uint16_t* dst = rkv::layer_ptrs(c->g, l).normw;
+    hipError_t e = hipMemcpyAsync(dst, wq_bf16, bytes, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(dst + c->p.head_dim, wk_bf16, bytes, hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "norm weight copy");
+    c->norm_eps[l] = eps;
+  }
+  g_err.clear();
   return RKV_OK;
 }
 

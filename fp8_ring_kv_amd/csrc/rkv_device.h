@@ -32,7 +32,7 @@ struct Geom {
   size_t consts;        // offset of the constants block (double omega/(2 pi) table)
   size_t layer0;        // offset of layer 0
   size_t layer_bytes;   // stride between layers
-  size_t off_codes_k, off_codes_v, off_scale_k, off_scale_v, off_slot_pos, off_state, off_vmax;
+  size_t off_codes_k, off_codes_v, off_scale_k, off_scale_v, off_slot_pos, off_state, off_vmax, off_normw;
   int32_t n_layers, n_slots, n_pad, n_tiles, n_heads, head_dim;
   float margin;
 };
@@ -46,6 +46,7 @@ struct LayerPtrs {
   int32_t* state;  // {head, n_valid, top ticket counter, 0}, sub-counters at kTicketStride * (1 + j)
   uint32_t* vmax;  // [H][kSub] largest value scale written since the reset (fp32
                    // bits); the head's bound is the max over its kSub entries
+  uint16_t* normw; // bf16 [2][D]: RMS-norm weights of the queries, then of the keys
 };
 
 __host__ __device__ inline LayerPtrs layer_ptrs(const Geom& g, int layer) {
@@ -58,6 +59,7 @@ __host__ __device__ inline LayerPtrs layer_ptrs(const Geom& g, int layer) {
   p.slot_pos = reinterpret_cast<int32_t*>(b + g.off_slot_pos);
   p.state = reinterpret_cast<int32_t*>(b + g.off_state);
   p.vmax = reinterpret_cast<uint32_t*>(b + g.off_vmax);
+  p.normw = reinterpret_cast<uint16_t*>(b + g.off_normw);
   return p;
 }
 
@@ -189,6 +191,28 @@ __device__ inline float dpp_f(float v) {
 // Max over each aligned group of W lanes (W = 2 .. 64), with DPP steps inside
 // 16-lane rows (rotate by 8, mirror within 8, swap within 4 and 2) and lane
 // swaps across rows (permlane16/32 swap): no LDS round trips.
+// Sum over each aligned group of W lanes (W = 2 .. 16), with the same DPP
+// steps as group_max; every lane of the group gets the total.
+template <int W>
+__device__ inline float group_sum(float v) {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16, "group width");
+  if constexpr (W >= 16) v += dpp_f<0x128>(v);  // row_ror:8
+  if constexpr (W >= 8) v += dpp_f<0x141>(v);   // row_half_mirror
+  if constexpr (W >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f<0xB1>(v);                          // quad_perm [1,0,3,2]
+  return v;
+}
+
+// RMS normalization of one row held by a group of lanes (the fused
+// pre-attention norm): x * w / sqrt(mean(x^2) + eps), squares summed in fp32.
+// ss is this lane's sum of squares; the group's total is over the D
+// elements of the row.  The factor is the hardware reciprocal square root
+// (within about 1 ulp).
+template <int W>
+__device__ inline float rms_factor(float ss, float inv_d, float eps) {
+  return __builtin_amdgcn_rsqf(group_sum<W>(ss) * inv_d + eps);
+}
+
 template <int W>
 __device__ inline float group_max(float v) {
   static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "group width");

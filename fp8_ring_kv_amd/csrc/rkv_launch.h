@@ -33,16 +33,19 @@ hipError_t launch_probe_mfma(int workgroups, int iters, float* sink, hipStream_t
 hipError_t launch_probe_stream(void* buf, size_t bytes, hipStream_t s);
 hipError_t launch_init_consts(const Geom& g, const double* turns, int n, hipStream_t s);
 hipError_t launch_reset(const Geom& g, int layer_lo, int layer_hi, hipStream_t s);
+// wk (and wq below): the layer's RMS-norm weights (bf16 [D]) of the fused
+// pre-attention norm, null when it is off; eps its epsilon.
 hipError_t launch_write(const Geom& g, int layer, const void* k, const void* v, const int32_t* pos,
-                        int n, hipStream_t s);
+                        int n, const uint16_t* wk, float eps, hipStream_t s);
 hipError_t launch_rotate(const Geom& g, int layer_lo, int layer_hi, int32_t delta,
                          const float* cosv, const float* sinv, hipStream_t s);
 hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void* q,
-                         const int32_t* q_pos, int n_q, void* out, hipStream_t s);
+                         const int32_t* q_pos, int n_q, void* out, const uint16_t* wq, float eps,
+                         hipStream_t s);
 // Write, then attention, with the query preparation in the write's launch.
 hipError_t launch_write_attend(const Geom& g, const AttnWs& ws, int layer, const void* k, const void* v,
                                const int32_t* pos, int n, const void* q, const int32_t* q_pos, int n_q,
-                               void* out, hipStream_t s);
+                               void* out, const uint16_t* wq, const uint16_t* wk, float eps, hipStream_t s);
 
 // Grid of the write: `groups` 16-slot groups (a run of n slots meets at most
 // n/16 + 2 of them) times n_heads / hg head groups of hg heads.  Two heads per

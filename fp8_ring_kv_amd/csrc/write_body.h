@@ -25,10 +25,13 @@ namespace rkv {
 // cos/sin serve all of them.
 // The body takes its workgroup coordinates (bx, by) in a (gx, gy) grid as
 // arguments, so that a launch can also run it on part of its workgroups.
+// wk: the layer's key RMS-norm weights (bf16 [D], shared by the heads) when
+// the fused pre-attention norm is on, else null; eps its epsilon.
 template <int D, int HG>
 __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4* __restrict__ k,
                                            const uint4* __restrict__ v, const int32_t* __restrict__ pos,
-                                           int n, int bx, int by, int gx, int gy) {
+                                           int n, const uint16_t* __restrict__ wk, float eps, int bx, int by,
+                                           int gx, int gy) {
   constexpr int LPR = D / 8;  // lanes per token row
   __shared__ uint2 vcodes[HG][16][LPR];
   __shared__ float vmx[HG][16];
@@ -80,11 +83,15 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
   const double* turns = omega_turns(g);
 #pragma unroll
   for (int m = 0; m < 4; ++m) tw[m] = turns[4 * lane + m];
+  // the norm weights of this lane's 8 elements (the same for every head)
+  uint4 wkv = make_uint4(0u, 0u, 0u, 0u);
+  if (wk != nullptr) wkv = reinterpret_cast<const uint4*>(wk)[lane];
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh)
     asm volatile("" ::"v"(kw[hh].x), "v"(kw[hh].y), "v"(kw[hh].z), "v"(kw[hh].w), "v"(vw[hh].x), "v"(vw[hh].y),
                  "v"(vw[hh].z), "v"(vw[hh].w));
-  asm volatile("" ::"v"(p), "v"(tw[0]), "v"(tw[1]), "v"(tw[2]), "v"(tw[3]) : "memory");
+  asm volatile("" ::"v"(p), "v"(tw[0]), "v"(tw[1]), "v"(tw[2]), "v"(tw[3]), "v"(wkv.x), "v"(wkv.y), "v"(wkv.z),
+               "v"(wkv.w) : "memory");
   const int wgi = by * gx + bx, nwg = gx * gy;
   const bool two_level = nwg > kTicketSplitMin;
   const int sub = wgi % kTicketSub;
@@ -100,8 +107,18 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
 
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh) {
-    const float x[8] = {bf16_lo(kw[hh].x), bf16_hi(kw[hh].x), bf16_lo(kw[hh].y), bf16_hi(kw[hh].y),
-                        bf16_lo(kw[hh].z), bf16_hi(kw[hh].z), bf16_lo(kw[hh].w), bf16_hi(kw[hh].w)};
+    float x[8] = {bf16_lo(kw[hh].x), bf16_hi(kw[hh].x), bf16_lo(kw[hh].y), bf16_hi(kw[hh].y),
+                  bf16_lo(kw[hh].z), bf16_hi(kw[hh].z), bf16_lo(kw[hh].w), bf16_hi(kw[hh].w)};
+    if (wk != nullptr) {  // fused RMS norm of the key row, before RoPE
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+      const float r = rms_factor<LPR>(ss, 1.f / D, eps);
+      const float w[8] = {bf16_lo(wkv.x), bf16_hi(wkv.x), bf16_lo(wkv.y), bf16_hi(wkv.y),
+                          bf16_lo(wkv.z), bf16_hi(wkv.z), bf16_lo(wkv.w), bf16_hi(wkv.w)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = x[e] * r * w[e];
+    }
     const float u[8] = {bf16_lo(vw[hh].x), bf16_hi(vw[hh].x), bf16_lo(vw[hh].y), bf16_hi(vw[hh].y),
                         bf16_lo(vw[hh].z), bf16_hi(vw[hh].z), bf16_lo(vw[hh].w), bf16_hi(vw[hh].w)};
     float y[8];

@@ -96,6 +96,8 @@ typedef struct {
  *                                      internal to the write kernel (a top
  *                                      counter at [2], 8 sub-counters at
  *                                      [64 (1 + j)]), zero between calls.
+ *   normw    bf16 [2][D]              RMS-norm weights of the queries, then
+ *                                      of the keys (ring_cache_set_qk_norm)
  *   vmax     f32 [H][8]               per head, the largest value scale
  *                                      written since the last reset (an upper
  *                                      bound of every cached value scale) is
@@ -172,6 +174,28 @@ int cache_attend(rkv_cache* c, int32_t layer, const void* q_bf16, const int32_t*
 int cache_write_attend(rkv_cache* c, int32_t layer, const void* k_bf16, const void* v_bf16,
                        const int32_t* pos, int32_t n, const void* q_bf16, const int32_t* q_pos,
                        int32_t n_q, void* out_bf16, hipStream_t stream);
+
+/* Fused pre-attention RMS norm (§4.4 "Fused pre-attention", Appendix G:
+ * each block RMS-normalizes Q and K, then applies RoPE, then quantizes and
+ * writes).  Once set for a layer, every write of that layer
+ * (cache_write_rope_fp8, cache_write_attend) normalizes each (token, head)
+ * key row, and every attention call (cache_attend, cache_write_attend) each
+ * query row, before RoPE:
+ *   y_d = x_d * w_d / sqrt(mean over d of x_d^2 + eps)
+ * in fp32 (squares summed in fp32; the factor is the hardware reciprocal
+ * square root).  Values are not normalized.
+ * wq_bf16, wk_bf16: device bf16 [head_dim] weight vectors, each shared by all
+ * heads, copied into the cache buffer on `stream` (device to device; the
+ * caller may reuse them once the stream has passed the copy).  Both null:
+ * the norm is off for the layer(s), the default.  layer -1: every layer.
+ * eps: finite and > 0.  The setting is host state of the handle, read when
+ * each later call is enqueued (calls already enqueued or captured keep the
+ * setting they were made with).
+ * Errors: RKV_EINVAL for a null cache, a layer out of range, exactly one
+ * null weight pointer, a pointer not 2-byte aligned, or eps not finite and
+ * > 0; RKV_EHIP if a copy cannot be enqueued. */
+int ring_cache_set_qk_norm(rkv_cache* c, int32_t layer, const void* wq_bf16, const void* wk_bf16, float eps,
+                           hipStream_t stream);
 
 /* Message for the last error on the calling thread ("" if none). */
 const char* rkv_last_error(void);

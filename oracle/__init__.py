@@ -18,6 +18,8 @@ Diffusion Transformer for Real-Time Conversation" (arXiv:2611.05642):
   with RoPE and per-(token, head) FP8 quantization fused in (§4.1, §4.3, §4.4),
   and the delta rotation of every valid cached key at a position reset
   (§4.2, Appendix G).
+* ``norm`` -- RMS normalization of query and key rows before RoPE (the fused
+  pre-attention norm, §4.4).
 * ``attend`` -- attention of new queries over every valid slot, in three
   precisions: exact (no query quantization), method (queries quantized per
   call, §4.3), and emul (the device kernel's declared numerics).
@@ -34,4 +36,4 @@ two-term probability split has closed forms and an error bound; and its
 e4m3 rounding is the codec pinned against torch's cast.
 """
 
-from . import e4m3, rope, ring, attend, bf16  # noqa: F401
+from . import e4m3, rope, ring, attend, bf16, norm  # noqa: F401
