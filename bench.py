@@ -12,7 +12,7 @@ cache starts full with its ring head at slot 3,100 (8,888 tokens written).
 Prints one JSON line.  `value` is microseconds per step (= per attention call
 with its cache work, resets amortized).  The steps run first with eager
 launches (`components.eager_us_per_step`); when --steps is a whole number of
-42-step reset periods (the default 84), the same steps are then captured as
+42-step reset periods (the default 168), the same steps are then captured as
 one HIP graph per period (the device-side write position makes every call
 capturable) and replayed, and `value` is the replayed time (`launch` says
 which).  Per-operation times come from separate HIP-event-timed loops on the
@@ -47,7 +47,7 @@ PEAK_HBM_GBPS = 8000.0
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=84)
+    ap.add_argument("--steps", type=int, default=168)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--precision", choices=["precise", "fast"], default="precise")
     ap.add_argument("--no-cpu-baseline", action="store_true")
