@@ -23,7 +23,7 @@ __all__ = [
     "rkv_params", "rkv_layout", "RkvError", "lib", "lib_path",
     "ring_cache_bytes", "ring_cache_create", "ring_cache_destroy", "ring_cache_reset",
     "ring_cache_layout", "cache_write_rope_fp8", "cache_delta_rotate", "cache_attend",
-    "cache_write_attend", "ring_cache_set_qk_norm",
+    "cache_write_attend", "ring_cache_set_qk_norm", "ring_cache_calibrate_static",
     "rkv_last_error", "rkv_probe_fp8_mfma", "rkv_probe_stream", "RingCache",
 ]
 
@@ -106,6 +106,8 @@ def lib() -> ctypes.CDLL:
     L.rkv_last_error.argtypes = []
     L.rkv_last_error.restype = ctypes.c_char_p
     L.ring_cache_set_qk_norm.argtypes = [VP, I32, VP, VP, ctypes.c_float, VP]
+    L.ring_cache_calibrate_static.argtypes = [VP, I32, ctypes.c_float, VP]
+    L.ring_cache_calibrate_static.restype = ctypes.c_int
     L.ring_cache_set_qk_norm.restype = ctypes.c_int
     L.rkv_probe_fp8_mfma.argtypes = [I32, I32, VP, VP]
     L.rkv_probe_fp8_mfma.restype = ctypes.c_int
@@ -186,6 +188,12 @@ def ring_cache_set_qk_norm(handle: int, layer: int, wq: int, wk: int, eps: float
                                       eps, ctypes.c_void_p(stream))
     if rc != RKV_OK:
         raise RkvError(rc, "ring_cache_set_qk_norm")
+
+
+def ring_cache_calibrate_static(handle: int, layer: int, margin: float, stream: int) -> None:
+    rc = lib().ring_cache_calibrate_static(ctypes.c_void_p(handle), layer, margin, ctypes.c_void_p(stream))
+    if rc != RKV_OK:
+        raise RkvError(rc, "ring_cache_calibrate_static")
 
 
 # ---- measurement aids (include/rkv_probe.h) ----------------------------------
@@ -270,6 +278,17 @@ class RingCache:
             _check(t, torch.bfloat16, (self.head_dim,), nm)
         self._norm_refs = (wq, wk)
         ring_cache_set_qk_norm(self.handle, layer, wq.data_ptr(), wk.data_ptr(), eps, _stream_handle(stream))
+
+    def calibrate_static(self, layer: int, margin: float = 1.5, stream=None):
+        """Switch `layer` (-1: all) to static per-head scales from the valid cache's amax x margin."""
+        ring_cache_calibrate_static(self.handle, layer, margin, _stream_handle(stream))
+
+    def static_scales(self, layer: int) -> torch.Tensor:
+        """[2][H] float32: static key and value scales (zeros before calibration)."""
+        lay = self.layout(layer)
+        base = lay.vmax + ((4 * 8 * self.n_heads + 255) // 256) * 256
+        base += ((2 * self.head_dim * 2 + 255) // 256) * 256
+        return self._view(base, 4 * 2 * self.n_heads, torch.float32).view(2, self.n_heads)
 
     def rotate(self, layer: int, delta: int, stream=None):
         cache_delta_rotate(self.handle, layer, int(delta), _stream_handle(stream))

@@ -60,11 +60,86 @@ __global__ void reset_kernel(Geom g, int layer_lo) {
     for (int j = (int)threadIdx.x; j < kStateRegionInts; j += (int)blockDim.x) L.state[j] = 0;
   if (blockIdx.x == 0)
     for (int j = (int)threadIdx.x; j < g.n_heads * kSub; j += (int)blockDim.x) L.vmax[j] = 0u;
+  // back to per-(token, head) scales until the next calibration
+  if (blockIdx.x == 0)
+    for (int j = (int)threadIdx.x; j <= 2 * g.n_heads; j += (int)blockDim.x) L.stat[j] = 0.f;
 }
 
 hipError_t launch_reset(const Geom& g, int layer_lo, int layer_hi, hipStream_t s) {
   dim3 grid((g.n_pad + 255) / 256, layer_hi - layer_lo);
   hipLaunchKernelGGL(reset_kernel, grid, dim3(256), 0, s, g, layer_lo);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Static-scale calibration, the pages' own scale mode (Appendix G; §4.3 "FP8
+// at write"): per (layer, head), amax = the largest magnitude of the
+// dequantized keys (values) over the valid slots, s = fp32(margin amax / 448);
+// then the layer's flag is set and later writes quantize with these scales
+// and reset rotations keep them.  One workgroup per (head, layer) scans the
+// head's codes 16 bytes per thread.  The products code * scale are exact in
+// double precision and the scale is formed as margin * amax / 448 in double,
+// rounded once to float.
+__device__ inline double max16_scaled(uint4 w, const float* sc, bool per_elem, double m) {
+  float x[16];
+  unpack4_fp8(w.x, x[0], x[1], x[2], x[3]);
+  unpack4_fp8(w.y, x[4], x[5], x[6], x[7]);
+  unpack4_fp8(w.z, x[8], x[9], x[10], x[11]);
+  unpack4_fp8(w.w, x[12], x[13], x[14], x[15]);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) m = fmax(m, fabs((double)x[e]) * (double)sc[per_elem ? e : 0]);
+  return m;
+}
+
+__global__ __launch_bounds__(256) void calibrate_kernel(Geom g, int layer_lo, float margin) {
+  __shared__ double red[2][256];
+  const LayerPtrs L = layer_ptrs(g, layer_lo + (int)blockIdx.y);
+  const int h = (int)blockIdx.x, H = g.n_heads, D = g.head_dim, N = g.n_slots, NP = g.n_pad;
+  const int head = L.state[0], nv = L.state[1];
+  int a = head - nv;
+  if (a < 0) a += N;
+  auto valid = [&](int slot) {
+    int rel = slot - a;
+    if (rel < 0) rel += N;
+    return slot < N && rel < nv;
+  };
+  const int CH = D / 16;  // 16-byte chunks per key row
+  double mk = 0.0, mv = 0.0;
+  for (int idx = (int)threadIdx.x; idx < NP * CH; idx += 256) {  // keys: slot-major rows
+    const int slot = idx / CH, c = idx % CH;
+    if (!valid(slot)) continue;
+    const uint4 w = *reinterpret_cast<const uint4*>(L.codes_k + ((size_t)h * NP + slot) * D + 16 * c);
+    mk = max16_scaled(w, L.scale_k + (size_t)h * NP + slot, false, mk);
+  }
+  for (int idx = (int)threadIdx.x; idx < g.n_tiles * D * 4; idx += 256) {  // values: [tile][d][64 slots]
+    const int tile = idx / (D * 4), d = (idx / 4) % D, qtr = idx % 4;
+    const int s0 = kTile * tile + 16 * qtr;
+    const uint4 w = *reinterpret_cast<const uint4*>(L.codes_v + (((size_t)h * g.n_tiles + tile) * D + d) * kTile +
+                                                    16 * qtr);
+    float sc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc[e] = valid(s0 + e) ? L.scale_v[(size_t)h * NP + s0 + e] : 0.f;
+    mv = max16_scaled(w, sc, true, mv);
+  }
+  red[0][threadIdx.x] = mk;
+  red[1][threadIdx.x] = mv;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      red[0][threadIdx.x] = fmax(red[0][threadIdx.x], red[0][threadIdx.x + w]);
+      red[1][threadIdx.x] = fmax(red[1][threadIdx.x], red[1][threadIdx.x + w]);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    L.stat[h] = (float)((double)margin * red[0][0] / (double)kE4M3Max);
+    L.stat[H + h] = (float)((double)margin * red[1][0] / (double)kE4M3Max);
+    if (h == 0) reinterpret_cast<int*>(L.stat)[2 * H] = 1;
+  }
+}
+
+hipError_t launch_calibrate(const Geom& g, int layer_lo, int layer_hi, float margin, hipStream_t s) {
+  hipLaunchKernelGGL(calibrate_kernel, dim3(g.n_heads, layer_hi - layer_lo), dim3(256), 0, s, g, layer_lo, margin);
   return hipGetLastError();
 }
 
@@ -131,6 +206,8 @@ __global__ __launch_bounds__(256) void rotate_kernel(Geom g, int layer_lo, int32
   const LayerPtrs L = layer_ptrs(g, layer_lo + (int)blockIdx.y);
   const int N = g.n_slots, NP = g.n_pad;
   const int head = L.state[0], nv = L.state[1];
+  // the pages' static-scale mode: every key keeps its scale, values beyond it saturate
+  const bool keep = reinterpret_cast<const int*>(L.stat)[2 * g.n_heads] != 0;
   int a = head - nv;
   if (a < 0) a += N;
   const int lane = threadIdx.x % LPR;
@@ -175,7 +252,7 @@ __global__ __launch_bounds__(256) void rotate_kernel(Geom g, int layer_lo, int32
       am = fmaxf(am, fmaxf(fabsf(y[2 * m]), fabsf(y[2 * m + 1])));
     }
     am = group_max<LPR>(am);
-    const float sn2 = am * g.margin / kE4M3Max;
+    const float sn2 = keep ? sc[k] : am * g.margin / kE4M3Max;
     const float rn = sn2 > 0.f ? 1.f / sn2 : 0.f;
     uint4 o;
     uint32_t* ow = &o.x;

@@ -101,6 +101,8 @@ Plan make_plan(const rkv_params* p) {
   o = align_up(o + H * rkv::kSub * 4, kAlign);
   g.off_normw = o;
   o = align_up(o + 2 * D * 2, kAlign);
+  g.off_static = o;
+  o = align_up(o + (2 * H + 1) * 4, kAlign);
   g.layer_bytes = o;
 
   size_t w = g.layer0 + (size_t)p->n_layers * g.layer_bytes;
@@ -348,6 +350,17 @@ int ring_cache_set_qk_norm(rkv_cache* c, int32_t layer, const void* wq_bf16, con
     if (e != hipSuccess) return hip_fail(e, "norm weight copy");
     c->norm_eps[l] = eps;
   }
+  g_err.clear();
+  return RKV_OK;
+}
+
+int ring_cache_calibrate_static(rkv_cache* c, int32_t layer, float margin, hipStream_t stream) {
+  if (!c) return fail(RKV_EINVAL, "cache is null");
+  int lo, hi;
+  if (int r = layer_range(c, layer, true, &lo, &hi)) return r;
+  if (!(margin > 0.f) || !(margin <= 64.f)) return fail(RKV_EINVAL, "margin must be in (0, 64]");
+  hipError_t e = rkv::launch_calibrate(c->g, lo, hi, margin, stream);
+  if (e != hipSuccess) return hip_fail(e, "calibrate kernel launch");
   g_err.clear();
   return RKV_OK;
 }

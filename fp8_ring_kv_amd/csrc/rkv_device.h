@@ -32,7 +32,7 @@ struct Geom {
   size_t consts;        // offset of the constants block (double omega/(2 pi) table)
   size_t layer0;        // offset of layer 0
   size_t layer_bytes;   // stride between layers
-  size_t off_codes_k, off_codes_v, off_scale_k, off_scale_v, off_slot_pos, off_state, off_vmax, off_normw;
+  size_t off_codes_k, off_codes_v, off_scale_k, off_scale_v, off_slot_pos, off_state, off_vmax, off_normw, off_static;
   int32_t n_layers, n_slots, n_pad, n_tiles, n_heads, head_dim;
   float margin;
 };
@@ -47,6 +47,8 @@ struct LayerPtrs {
   uint32_t* vmax;  // [H][kSub] largest value scale written since the reset (fp32
                    // bits); the head's bound is the max over its kSub entries
   uint16_t* normw; // bf16 [2][D]: RMS-norm weights of the queries, then of the keys
+  float* stat;     // [2][H] static per-head scales (keys, then values), then an int
+                   // flag at [2H]: nonzero once calibrated (the pages' scale mode)
 };
 
 __host__ __device__ inline LayerPtrs layer_ptrs(const Geom& g, int layer) {
@@ -60,6 +62,7 @@ __host__ __device__ inline LayerPtrs layer_ptrs(const Geom& g, int layer) {
   p.state = reinterpret_cast<int32_t*>(b + g.off_state);
   p.vmax = reinterpret_cast<uint32_t*>(b + g.off_vmax);
   p.normw = reinterpret_cast<uint16_t*>(b + g.off_normw);
+  p.stat = reinterpret_cast<float*>(b + g.off_static);
   return p;
 }
 

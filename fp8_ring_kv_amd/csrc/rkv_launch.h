@@ -33,6 +33,8 @@ hipError_t launch_probe_mfma(int workgroups, int iters, float* sink, hipStream_t
 hipError_t launch_probe_stream(void* buf, size_t bytes, hipStream_t s);
 hipError_t launch_init_consts(const Geom& g, const double* turns, int n, hipStream_t s);
 hipError_t launch_reset(const Geom& g, int layer_lo, int layer_hi, hipStream_t s);
+// Static per-head scales from the valid cache of each layer in [layer_lo, layer_hi).
+hipError_t launch_calibrate(const Geom& g, int layer_lo, int layer_hi, float margin, hipStream_t s);
 // wk (and wq below): the layer's RMS-norm weights (bf16 [D]) of the fused
 // pre-attention norm, null when it is off; eps its epsilon.
 hipError_t launch_write(const Geom& g, int layer, const void* k, const void* v, const int32_t* pos,

@@ -40,6 +40,8 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
   const int N = g.n_slots, NP = g.n_pad, H = g.n_heads;
   const int head = L.state[0];
   const int nvalid = L.state[1];
+  // the pages' static per-(layer, head) scales, once calibrated
+  const bool smode = reinterpret_cast<const int*>(L.stat)[2 * H] != 0;
   const int h0 = by * HG;
   const int NG = (N + 15) / 16;  // 16-slot groups of the ring (the last may be short)
   const int G = (head / 16 + bx) % NG;
@@ -136,10 +138,22 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
     // fp32 RoPE results (a rounding away from the exact rotation already):
     // y * (1/s).  Values are raw bf16, whose quotients often sit next to e4m3
     // midpoints: the exact quotient code (vquot_row).
-    const float amk = ak * g.margin, amv = av * g.margin;
-    const float sk = div448(amk), sv = div448(amv);
-    const float rk = recip_scale(sk);
-    const VQuot qv = vquot_row(amv, sv);
+    float sk, sv, rk;
+    VQuot qv;
+    if (smode) {  // static scales: correctly rounded quotients, saturating at +-448
+      sk = L.stat[h0 + hh];
+      sv = L.stat[H + h0 + hh];
+      rk = recip_scale(sk);
+      qv.s = sv;
+      qv.r = recip_scale(sv);
+      qv.f = 1.f;
+    } else {
+      const float amk = ak * g.margin, amv = av * g.margin;
+      sk = div448(amk);
+      sv = div448(amv);
+      rk = recip_scale(sk);
+      qv = vquot_row(amv, sv);
+    }
     uint2 ck, cv;
     ck.x = pack2_fp8<false>(quant_mul(y[0], rk), quant_mul(y[1], rk), 0u);
     ck.x = pack2_fp8<true>(quant_mul(y[2], rk), quant_mul(y[3], rk), ck.x);

@@ -98,6 +98,9 @@ typedef struct {
  *                                      [64 (1 + j)]), zero between calls.
  *   normw    bf16 [2][D]              RMS-norm weights of the queries, then
  *                                      of the keys (ring_cache_set_qk_norm)
+ *   static   f32 [2][H], i32          static scales of the keys, then of the
+ *                                      values, and a flag (nonzero once
+ *                                      calibrated: ring_cache_calibrate_static)
  *   vmax     f32 [H][8]               per head, the largest value scale
  *                                      written since the last reset (an upper
  *                                      bound of every cached value scale) is
@@ -196,6 +199,22 @@ int cache_write_attend(rkv_cache* c, int32_t layer, const void* k_bf16, const vo
  * > 0; RKV_EHIP if a copy cannot be enqueued. */
 int ring_cache_set_qk_norm(rkv_cache* c, int32_t layer, const void* wq_bf16, const void* wk_bf16, float eps,
                            hipStream_t stream);
+
+/* The pages' own scale mode (§4.3 "FP8 at write", Appendix G: scales per
+ * (layer, head), calibrated once per session from the amax of the cache the
+ * first steps filled, times a margin; values beyond them saturate; a reset
+ * rotation keeps them and clamps).  For each layer (-1: all) this enqueues a
+ * kernel that takes, per head, the largest magnitude of the dequantized keys
+ * and of the values over the valid slots and sets the static scales
+ * s = fp32(margin * amax / 448) (amax and the product in double precision).
+ * From then on, every write of the layer quantizes with these scales
+ * (e4m3 of the correctly rounded y / s, saturating) and stores them as the
+ * slots' scales, and every delta rotation keeps each key's scale and clamps;
+ * the attention is unchanged.  ring_cache_reset returns the layer to
+ * per-(token, head) scales.  The mode is device state (graph-capturable).
+ * margin in (0, 64] (the pages use 1.5).  Errors: RKV_EINVAL for a null
+ * cache, a layer out of range or a bad margin; RKV_EHIP if the launch fails. */
+int ring_cache_calibrate_static(rkv_cache* c, int32_t layer, float margin, hipStream_t stream);
 
 /* Message for the last error on the calling thread ("" if none). */
 const char* rkv_last_error(void);

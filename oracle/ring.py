@@ -55,6 +55,10 @@ class RingState:
     scale_k: np.ndarray = field(default=None)
     scale_v: np.ndarray = field(default=None)
     vmax: np.ndarray = field(default=None)  # per head: largest s_v written since the reset
+    # static per-(layer, head) scales of the pages' own scale mode, [H] each
+    # (float64 holding fp32 values); None: per-(token, head) amax scales
+    static_k: np.ndarray = field(default=None)
+    static_v: np.ndarray = field(default=None)
 
     def __post_init__(self):
         n, h, d = self.n_slots, self.n_heads, self.head_dim
@@ -75,7 +79,9 @@ class RingState:
         return RingState(self.n_slots, self.n_heads, self.head_dim, self.rope_base, self.margin,
                          self.head, self.n_valid, self.slot_pos.copy(), self.codes_k.copy(),
                          self.codes_v.copy(), self.scale_k.copy(), self.scale_v.copy(),
-                         self.vmax.copy())
+                         self.vmax.copy(),
+                         None if self.static_k is None else self.static_k.copy(),
+                         None if self.static_v is None else self.static_v.copy())
 
 
 def valid_slots(st: RingState) -> np.ndarray:
@@ -105,8 +111,12 @@ def write(st: RingState, k: np.ndarray, v: np.ndarray, pos: np.ndarray) -> None:
     if k.shape != (n, st.n_heads, st.head_dim) or v.shape != k.shape or pos.shape != (n,):
         raise ValueError("write: shape mismatch")
     k_rot = rope(k, pos, st.rope_base)  # [n, H, D]
-    ck, sk = e4m3.quantize_rows(k_rot, st.margin)  # [n, H, D], [n, H]
-    cv, sv = e4m3.quantize_rows(v, st.margin)
+    if st.static_k is None:
+        ck, sk = e4m3.quantize_rows(k_rot, st.margin)  # [n, H, D], [n, H]
+        cv, sv = e4m3.quantize_rows(v, st.margin)
+    else:
+        ck, sk = quantize_static(k_rot, st.static_k)
+        cv, sv = quantize_static(v, st.static_v)
     slots = write_slots(st, n)
     st.codes_k[:, slots, :] = np.transpose(ck, (1, 0, 2))
     st.codes_v[:, slots, :] = np.transpose(cv, (1, 0, 2))
@@ -131,18 +141,49 @@ def rotate(st: RingState, delta: int) -> None:
     c, s = delta_angles(st.head_dim, delta, st.rope_base)
     x = e4m3.decode(st.codes_k[:, slots, :]) * st.scale_k[:, slots][..., None]
     y = rotate_pairs(x, c, s)
-    ck, sk = e4m3.quantize_rows(y, st.margin)
+    if st.static_k is None:
+        ck, sk = e4m3.quantize_rows(y, st.margin)
+    else:  # the pages' own mode: the same scale, values beyond it saturate
+        sk = st.scale_k[:, slots]
+        ck = e4m3.encode(y / np.where(sk > 0, sk, 1.0)[..., None])
     st.codes_k[:, slots, :] = ck
     st.scale_k[:, slots] = sk
     st.slot_pos[slots] = st.slot_pos[slots] + delta
 
 
 def reset(st: RingState) -> None:
-    """Session reset: empty ring (head 0, no valid slots, positions 0, vmax 0)."""
+    """Session reset: empty ring (head 0, no valid slots, positions 0, vmax 0),
+    back to per-(token, head) scales until the next calibration."""
     st.head = 0
     st.n_valid = 0
     st.slot_pos[:] = 0
     st.vmax[:] = 0
+    st.static_k = st.static_v = None
+
+
+def quantize_static(y: np.ndarray, s_head: np.ndarray):
+    """Codes of [n, H, D] rows with one fixed scale per head: e4m3(y / s_h),
+    saturating at +-448 (values beyond the scale clip); scale 0 gives codes 0.
+    Returns (codes, per-row scales [n, H])."""
+    s = np.broadcast_to(np.asarray(s_head, dtype=np.float64)[None, :], y.shape[:2])
+    safe = np.where(s > 0, s, 1.0)
+    codes = e4m3.encode(np.where(s[..., None] > 0, y / safe[..., None], 0.0))
+    return codes, np.array(s)
+
+
+def calibrate_static(st: RingState, margin: float) -> None:
+    """The pages' scale calibration (Appendix G; §4.3 "FP8 at write"): per
+    head, s = fp32(margin * amax / 448) with amax the largest magnitude of the
+    dequantized keys (values) over the valid slots, then every later write
+    quantizes with these scales and a reset rotation keeps them."""
+    slots = valid_slots(st)
+    amk = np.zeros(st.n_heads)
+    amv = np.zeros(st.n_heads)
+    if slots.size:
+        amk = np.max(np.abs(dequant_k(st)[:, slots, :]), axis=(1, 2))
+        amv = np.max(np.abs(dequant_v(st)[:, slots, :]), axis=(1, 2))
+    st.static_k = (margin * amk / e4m3.E4M3_MAX).astype(np.float32).astype(np.float64)
+    st.static_v = (margin * amv / e4m3.E4M3_MAX).astype(np.float32).astype(np.float64)
 
 
 def dequant_k(st: RingState) -> np.ndarray:

@@ -1,0 +1,96 @@
+"""GPU parity of the pages' static-scale mode (Runway Characters paper §4.3
+"FP8 at write", Appendix G): calibration from the cache's amax x 1.5, static
+writes that saturate, reset rotations that keep the scales.  Bars as for the
+plain path: bookkeeping and the calibrated scales bit-exact, dequantized
+cache elements within 1 e4m3 ulp, attention within the 2e-2 / 2e-3 gates."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_ring_kv_amd as rkv
+from oracle import attend as oatt, ring as oring
+from oracle.bf16 import round_bf16
+from tests.gpu_common import DEV, assert_cache_matches, attn_errors, pos_dev, require_gpu, to_dev
+from workloads import Config, OutlierSpec, Stream, positions
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def test_static_session_matches_oracle():
+    cfg = Config("static", n_heads=4, head_dim=128, n_slots=700, chunk=300, seed=31,
+                 outliers=OutlierSpec(0.02, 8.0))
+    cache = rkv.RingCache(1, cfg.n_slots, cfg.n_heads, cfg.head_dim, cfg.chunk, rkv.RKV_PRECISE, device=DEV)
+    st = oring.RingState(cfg.n_slots, cfg.n_heads, cfg.head_dim)
+    s = Stream(cfg)
+    p0 = 0
+    for c in range(2):  # per-token scales first
+        _, k, v = s.chunk()
+        pos = positions(p0, cfg.chunk)
+        cache.write(0, to_dev(k), to_dev(v), pos_dev(pos))
+        oring.write(st, k.f64, v.f64, pos)
+        p0 += cfg.chunk
+    cache.calibrate_static(0, 1.5)
+    oring.calibrate_static(st, 1.5)
+    got = cache.static_scales(0).cpu().numpy().astype(np.float64)
+    # value scales are bit-exact (per-token value scales are).  A per-token key
+    # scale may differ by one ulp (amax of fp32 against float64 RoPE); times
+    # the margin 1.5 and rounded once more, that is at most two ulps of the
+    # static scale (2^-22 relative)
+    assert np.array_equal(got[1], st.static_v), (got[1], st.static_v)
+    assert np.all(np.abs(got[0] - st.static_k) <= st.static_k * 2.0 ** -22), (got[0] - st.static_k, st.static_k)
+    for c in range(3):  # static writes; the ring wraps and every slot is rewritten
+        _, k, v = s.chunk()
+        pos = positions(p0, cfg.chunk)
+        cache.write(0, to_dev(k), to_dev(v), pos_dev(pos))
+        oring.write(st, k.f64, v.f64, pos)
+        p0 += cfg.chunk
+        assert_cache_matches(cache, 0, st)
+    pre = st.copy()
+    sk_before = cache.scales(0)[0].clone()
+    cache.rotate(0, -600)
+    oring.rotate(st, -600)
+    assert_cache_matches(cache, 0, st, pre=pre)
+    assert torch.equal(cache.scales(0)[0], sk_before)  # the rotation kept every scale
+    q, _, _ = s.chunk()
+    qpos = positions(p0 - 600 - cfg.chunk, cfg.chunk)
+    out = cache.attend(0, to_dev(q), pos_dev(qpos)).float().cpu().numpy().astype(np.float64)
+    sig = oatt.sigma_v(st)
+    for name, ref in (("emul", round_bf16(oatt.attend_emul(st, q.f64, qpos))),
+                      ("exact", oatt.attend_exact(st, q.f64, qpos))):
+        rmax, rmean, nmax, nmean = attn_errors(out, ref, sig)
+        assert nmax < 2e-2 and nmean < 2e-3, (name, rmax, rmean, nmax, nmean)
+
+
+def test_reset_returns_to_per_token_scales():
+    cfg = Config("static_reset", n_heads=2, head_dim=64, n_slots=200, chunk=64, seed=32)
+    cache = rkv.RingCache(1, cfg.n_slots, cfg.n_heads, cfg.head_dim, cfg.chunk, device=DEV)
+    st = oring.RingState(cfg.n_slots, cfg.n_heads, cfg.head_dim)
+    s = Stream(cfg)
+    _, k, v = s.chunk()
+    cache.write(0, to_dev(k), to_dev(v), pos_dev(positions(0, 64)))
+    cache.calibrate_static(-1, 1.5)
+    cache.reset(0)
+    oring.reset(st)
+    assert not cache.static_scales(0).cpu().numpy().any()
+    _, k, v = s.chunk()
+    cache.write(0, to_dev(k), to_dev(v), pos_dev(positions(0, 64)))
+    oring.write(st, k.f64, v.f64, positions(0, 64))
+    assert_cache_matches(cache, 0, st)
+
+
+def test_calibrate_rejects_bad_arguments():
+    cache = rkv.RingCache(2, 64, 2, 64, 16, device=DEV)
+    L = rkv.lib()
+    vp, s = ctypes.c_void_p, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert L.ring_cache_calibrate_static(None, 0, 1.5, s) == rkv.RKV_EINVAL
+    assert L.ring_cache_calibrate_static(vp(cache.handle), 2, 1.5, s) == rkv.RKV_EINVAL
+    for m in (0.0, -1.0, 65.0, float("nan")):
+        assert L.ring_cache_calibrate_static(vp(cache.handle), 0, m, s) == rkv.RKV_EINVAL, m
+    assert "margin" in rkv.rkv_last_error()
