@@ -407,6 +407,12 @@ def main():
         comp["write_qk_norm_us"] = 1e3 * timed(lambda: cache.write(0, k0, v0, pos_pool[0]), r, stream)
         comp["write_attend_qk_norm_us"] = 1e3 * timed(wa, r, stream)
         cache.set_qk_norm(0, None, None)
+        # the pages' static per-(layer, head) scales: calibrate from the cache
+        # (amax x 1.5), then the same write and rotation with fixed scales
+        cache.calibrate_static(0, 1.5)
+        comp["write_static_us"] = 1e3 * timed(lambda: cache.write(0, k0, v0, pos_pool[0]), r, stream)
+        comp["rotate_static_1layer_us"] = 1e3 * timed(rot, max(20, r // 4), stream)
+        cache.reset(0)
         torch.cuda.synchronize()
         peaks = measured_peaks(stream)
 
