@@ -129,8 +129,10 @@ int ring_cache_destroy(rkv_cache* c);
 
 /* Session reset (§6 "Session start" clears the dynamic cache): set head,
  * n_valid, vmax and every slot position of one layer (or all layers when
- * layer == -1) to zero.  Codes and scales are left as they are; slots
- * outside the valid range are never read. */
+ * layer == -1) to zero, and return the layer to per-(token, head) scales
+ * (static scales are calibrated once per session: Appendix G).  Codes and
+ * per-slot scales are left as they are; slots outside the valid range are
+ * never read.  The fused Q/K norm setting (model weights) is kept. */
 int ring_cache_reset(rkv_cache* c, int32_t layer, hipStream_t stream);
 
 /* Fill *out with the byte offsets of `layer` inside the cache buffer. */
