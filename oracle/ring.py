@@ -13,7 +13,7 @@ Runway Characters paper:
   quantized.
 
 Readings taken where the pages are silent or differ from the hot path's
-statement (each is listed in DESIGN.md):
+statement:
 
 * scale rule: per-(token, head) s = fp32(margin * amax / 448), margin 1.0,
   amax over the RoPE'd K vector (float64, no intermediate rounding) and over
@@ -22,7 +22,12 @@ statement (each is listed in DESIGN.md):
   rule holds for every cached key after a reset (keeping the old scale with a
   margin of 1.0 would saturate about half of the keys);
 * the valid set is the cyclic slot range [head - n_valid, head); only valid
-  slots are rotated and their positions shifted.
+  slots are rotated and their positions shifted;
+* the pages' own scale mode (§4.3, Appendix G) is available after
+  ``calibrate_static``: per-head scales from the amax of the dequantized
+  cache over the valid slots times a margin, saturating writes with them,
+  and reset rotations that keep each key's scale and clamp; ``reset``
+  returns to per-(token, head) scales.
 
 State layout (canonical, independent of any device layout): codes [H][N][D]
 uint8, scales [H][N] float64 holding fp32 values, slot_pos [N] int64, and
