@@ -290,6 +290,13 @@ class RingCache:
         base += ((2 * self.head_dim * 2 + 255) // 256) * 256
         return self._view(base, 4 * 2 * self.n_heads, torch.float32).view(2, self.n_heads)
 
+    def static_flag(self, layer: int) -> bool:
+        """True once the layer is calibrated (static scales in use); reads the device."""
+        lay = self.layout(layer)
+        base = lay.vmax + ((4 * 8 * self.n_heads + 255) // 256) * 256
+        base += ((2 * self.head_dim * 2 + 255) // 256) * 256
+        return bool(self._view(base + 4 * 2 * self.n_heads, 4, torch.int32).item())
+
     def rotate(self, layer: int, delta: int, stream=None):
         cache_delta_rotate(self.handle, layer, int(delta), _stream_handle(stream))
 

@@ -8,8 +8,8 @@
 //
 // Two launches per call.  q_prep_kernel applies RoPE to the queries at their
 // positions (angles in double precision) and splits each (query, head) row
-// into one or two e4m3 terms with power-of-two scales, applied exactly by the
-// E8M0 scale operand of the matrix instruction.  attend_kernel then does the
+// into three e4m3 terms (one in fast mode) with power-of-two scales, applied
+// exactly by the E8M0 scale operand of the matrix instruction.  attend_kernel then does the
 // attention proper:
 //
 // Work: unit u = (head h, group qg of 128 queries), u = h * nqg + qg; each
@@ -40,10 +40,14 @@
 //      workgroups writes a partial (O, max, sum) per wave and the last
 //      workgroup to finish its part merges the partials.
 //
-// Probability scale: c_h = 448 / (4 vmax_h), vmax_h being the largest value
+// Probability scale: c_h = 448 / (64 vmax_h), vmax_h being the largest value
 // scale written to head h since the reset (kept by the write kernel).  The
-// running row maximum is raised only when a tile exceeds it by more than 2
-// (log2 units), so P <= 4 and P * s_v * c_h <= 448 always fits e4m3.
+// running row maximum is raised only when a tile exceeds it by more than 6
+// (log2 units), so P <= 64 and P * s_v * c_h <= 448 always fits e4m3.  (With
+// a headroom of 2 the raise, a wave-wide branch over 32 queries, ran on 54%
+// of the tiles of the 757 x 5,788 workload; with 6 on 14%.  The smaller c_h
+// moves only probabilities below about 1/100 of the row maximum into the
+// e4m3 subnormal range, where the second term still carries them.)
 #include <cmath>
 
 #include "rkv_launch.h"
@@ -58,8 +62,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;  // LDS byte, addressed without a generic pointer
 
 constexpr double kLog2e = 1.4426950408889634;  // log2(e)
-constexpr float kLazy = 2.f;  // log2 headroom of the running maximum
+constexpr float kLazy = 6.f;             // log2 headroom of the running maximum
+constexpr float kHeadroom = 64.f;        // 2^kLazy: c_h = 448 / (kHeadroom vmax_h)
 constexpr int kQG = 128;      // queries per unit: 4 waves x 32
+
+// Terms of the two precisions (TERMS = 2: precise, 1: fast).  Precise mode
+// splits each query into three e4m3 terms (q known to about 2^-12 relative:
+// with two, about 2^-8, a query whose outlier channels meet a key's moved
+// single outputs by up to 2.9e-2 of the value scale) and each probability
+// into two (hi + lo / 16); fast mode takes one of each.
+template <int TERMS>
+constexpr int q_terms() { return TERMS == 2 ? 3 : 1; }
 
 struct AttnArgs {
   Geom g;
@@ -355,7 +368,7 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
       acc[1][r] -= shift;
     }
   }
-  // P' <= 4 c_h and s_v c_h <= 112, so the conversions below never
+  // P' <= 64 c_h and s_v c_h <= 7, so the conversions below never
   // overflow (fp32 rounding a hair above 448 still rounds to 448 in e4m3).
   v8i ph, pl;
 #pragma unroll
@@ -400,7 +413,7 @@ struct __attribute__((aligned(16))) AttnSmem {
 
 // ---------------------------------------------------------------------------
 // Query preparation, one launch before the attention: RoPE at q_pos (angles
-// in double precision) and the split of each (query, head) row into TERMS
+// in double precision) and the split of each (query, head) row into QT
 // e4m3 terms with power-of-two scales: term t holds e4m3(y_t / 2^e_t) with
 // e_t the smallest exponent that fits the row (448 * 2^e_t >= amax), y_0 = y
 // and y_{t+1} the residual; the E8M0 operand 127 + e_t of the matrix
@@ -419,7 +432,7 @@ struct QPrepArgs {
 };
 
 // Body of one 256-thread workgroup number `block` of the preparation.
-template <int D, int TERMS>
+template <int D, int QT>
 __device__ inline void q_prep_body(const QPrepArgs& A, int block) {
   constexpr int TPR = 8;          // threads per row
   constexpr int EPT = D / TPR;    // elements per thread: 16 or 8
@@ -478,7 +491,7 @@ __device__ inline void q_prep_body(const QPrepArgs& A, int block) {
     }
   }
 #pragma unroll
-  for (int t = 0; t < TERMS; ++t) {
+  for (int t = 0; t < QT; ++t) {
     am = group_max<TPR>(am);
     const int e = am > 0.f ? pow2_exponent(am) : 0;
     uint32_t wd[EPT / 4];
@@ -490,7 +503,7 @@ __device__ inline void q_prep_body(const QPrepArgs& A, int block) {
       const float z0 = ldexpf(yy[0], -e);
       const uint32_t cw = pack2_fp8<false>(z0, ldexpf(yy[1], -e), __float_as_uint(z0));
       wd[c] = pack2_fp8<true>(ldexpf(yy[2], -e), ldexpf(yy[3], -e), cw);
-      if (t + 1 < TERMS) {
+      if (t + 1 < QT) {
         float d0, d1, d2, d3;
         unpack4_fp8(wd[c], d0, d1, d2, d3);
         yy[0] -= ldexpf(d0, e);
@@ -514,7 +527,7 @@ __device__ inline void q_prep_body(const QPrepArgs& A, int block) {
 
 template <int D, int TERMS>
 __global__ __launch_bounds__(256) void q_prep_kernel(QPrepArgs A) {
-  q_prep_body<D, TERMS>(A, (int)blockIdx.x);
+  q_prep_body<D, q_terms<TERMS>()>(A, (int)blockIdx.x);
 }
 
 // Write and query preparation in one launch (D = 128: both use 256-thread
@@ -538,7 +551,7 @@ __global__ __launch_bounds__(256) void write_prep_kernel(WritePrepArgs W) {
     write_rope_fp8_body<128, HG>(W.P.g, W.layer, W.k, W.v, W.pos, W.n, W.wk, W.P.eps, b % W.wgx, b / W.wgx, W.wgx,
                                  W.wgy);
   else
-    q_prep_body<128, TERMS>(W.P, b - nw);
+    q_prep_body<128, q_terms<TERMS>()>(W.P, b - nw);
 }
 
 __device__ inline v8i gload32(const uint8_t* p) {
@@ -736,12 +749,13 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
   const LayerPtrs L = layer_ptrs(g, A.layer);
   const int U = A.nqg * H;
   // This wave's 32 prepared queries of unit u (B operand of S^T = K Q^T).
-  v8i qf[TERMS][KS];
-  int qs[TERMS];
+  constexpr int QT = q_terms<TERMS>();
+  v8i qf[QT][KS];
+  int qs[QT];
   auto load_q = [&](int u) {
     const int h = u / A.nqg, qi = kQG * (u % A.nqg) + 32 * wave + li;
 #pragma unroll
-    for (int t = 0; t < TERMS; ++t) {
+    for (int t = 0; t < QT; ++t) {
       const size_t row = ((size_t)t * H + h) * A.ws.nq_pad + qi;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[t][ks] = gload32(A.ws.qcodes + row * D + 64 * ks + 32 * gq);
@@ -800,7 +814,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
 #pragma unroll
     for (int k2 = 0; k2 < kSub; ++k2) vm = max(vm, L.vmax[h * kSub + k2]);
     const float vmaxh = __uint_as_float(vm);
-    const float ch = vmaxh > 0.f ? kE4M3Max / (4.f * vmaxh) : 1.f;
+    const float ch = vmaxh > 0.f ? kE4M3Max / (kHeadroom * vmaxh) : 1.f;
     const float l2c = __log2f(ch);
     TileSrc src;
     src.kbase = L.codes_k + (size_t)h * NP * D;
@@ -838,7 +852,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
       VOp<D> vf;
       v16f sacc[2];
       read_k<D>(kf, lb, off);
-      qk<D, TERMS>(sacc, kf, qf, qs);
+      qk<D, QT>(sacc, kf, qf, qs);
       read_v<D>(vf, lb, off);
       // Only the first and last tiles of the valid range and the ring's last
       // tile (pad slots) can hold invalid slots: the others skip the mask.
@@ -863,7 +877,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
     } else {
       // Partial id gi + u is distinct for every (workgroup, unit) pair: ranges
       // are ordered, so a later workgroup never meets an earlier unit.  The
-      // partial is c_h O / l in fp16 (|c_h O / l| <= 448 * 112: the largest
+      // partial is c_h O / l in fp16 (|c_h O / l| <= 448 * 7: the largest
       // e4m3 value code times s_v c_h) plus the row's max and sum in fp32.
       // Partials travel with sc1 (device-coherent) buffer accesses, the cache
       // policy of agent-scope relaxed atomics: stores write through and loads
@@ -937,7 +951,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
 #pragma unroll
     for (int k2 = 0; k2 < kSub; ++k2) vm = max(vm, L.vmax[h * kSub + k2]);
     const float vmaxh = __uint_as_float(vm);
-    const float ch = vmaxh > 0.f ? kE4M3Max / (4.f * vmaxh) : 1.f;
+    const float ch = vmaxh > 0.f ? kE4M3Max / (kHeadroom * vmaxh) : 1.f;
     const PartRsrc pr = PartRsrc::make<D>(A.ws, G + U);
     uint32_t bits = (uint32_t)blocks & kAllBlocks<D>;
     for (int n = 0; bits; ++n) {  // the n-th block goes to wave n % 4

@@ -76,7 +76,9 @@ hipError_t launch_reset(const Geom& g, int layer_lo, int layer_hi, hipStream_t s
 // at write"): per (layer, head), amax = the largest magnitude of the
 // dequantized keys (values) over the valid slots, s = fp32(margin amax / 448);
 // then the layer's flag is set and later writes quantize with these scales
-// and reset rotations keep them.  One workgroup per (head, layer) scans the
+// and reset rotations requantize each head's keys with its key scale (a head
+// at amax 0 gets scale 0, which the write and the rotation read as "keep the
+// per-(token, head) rule").  One workgroup per (head, layer) scans the
 // head's codes 16 bytes per thread.  The products code * scale are exact in
 // double precision and the scale is formed as margin * amax / 448 in double,
 // rounded once to float.
@@ -206,14 +208,16 @@ __global__ __launch_bounds__(256) void rotate_kernel(Geom g, int layer_lo, int32
   const LayerPtrs L = layer_ptrs(g, layer_lo + (int)blockIdx.y);
   const int N = g.n_slots, NP = g.n_pad;
   const int head = L.state[0], nv = L.state[1];
-  // the pages' static-scale mode: every key keeps its scale, values beyond it saturate
-  const bool keep = reinterpret_cast<const int*>(L.stat)[2 * g.n_heads] != 0;
+  // the pages' static-scale mode: every key of a head is requantized with the
+  // head's scale, values beyond it saturate (a head calibrated at amax 0 has
+  // scale 0 and keeps the per-(token, head) rule)
+  const bool smode = reinterpret_cast<const int*>(L.stat)[2 * g.n_heads] != 0;
   int a = head - nv;
   if (a < 0) a += N;
   const int lane = threadIdx.x % LPR;
 
   uint4 w[kRPT];
-  float sc[kRPT];
+  float sc[kRPT], st[kRPT];
   size_t r[kRPT];
   int slot[kRPT];
   bool valid[kRPT];
@@ -227,11 +231,12 @@ __global__ __launch_bounds__(256) void rotate_kernel(Geom g, int layer_lo, int32
     valid[k] = h < g.n_heads && slot[k] < N && rel < nv;
     r[k] = (size_t)h * NP + slot[k];
     w[k] = make_uint4(0u, 0u, 0u, 0u);
-    sc[k] = 0.f;
+    sc[k] = st[k] = 0.f;
     if (valid[k]) {
       const u4v t = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(L.codes_k + r[k] * D + 16 * lane));
       w[k] = make_uint4(t[0], t[1], t[2], t[3]);
       sc[k] = L.scale_k[r[k]];
+      if (smode) st[k] = L.stat[h];
     }
   }
 #pragma unroll
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(256) void rotate_kernel(Geom g, int layer_lo, int32
       am = fmaxf(am, fmaxf(fabsf(y[2 * m]), fabsf(y[2 * m + 1])));
     }
     am = group_max<LPR>(am);
-    const float sn2 = keep ? sc[k] : am * g.margin / kE4M3Max;
+    const float sn2 = st[k] > 0.f ? st[k] : am * g.margin / kE4M3Max;
     const float rn = sn2 > 0.f ? 1.f / sn2 : 0.f;
     uint4 o;
     uint32_t* ow = &o.x;

@@ -46,8 +46,15 @@ struct Plan {
   rkv::Geom g;
   rkv::AttnWs ws;  // pointers filled relative to base 0 (offsets) until create
   size_t ws_parto, ws_partml, ws_sync, ws_qcodes, ws_qexp;
+  size_t part_bytes;  // fp16 split-unit partials: (units + workgroups) x 128 queries x D x 2 bytes
   size_t total;
 };
+
+// The attention kernel addresses the split-unit partials through 32-bit
+// buffer offsets and uses 2^30 as an offset past the end of the buffer, so
+// that buffer must stay below 1 GiB: (units + workgroups) * 256 * D < 2^30,
+// e.g. 256 heads x 14,000 queries at D = 128.
+constexpr size_t kMaxPartBytes = size_t(1) << 30;
 
 bool params_ok(const rkv_params* p, std::string* why) {
   if (!p) return *why = "params is null", false;
@@ -119,17 +126,18 @@ Plan make_plan(const rkv_params* p) {
   // the device real-time clock counts at 100 MHz
   pl.ws.wait_ticks = 100 * (p->attn_merge_wait_us < 0 ? 50 : p->attn_merge_wait_us);
   pl.ws_parto = w;
-  w = align_up(w + segs * 128 * D * 2, kAlign);
+  pl.part_bytes = segs * 128 * D * 2;
+  w = align_up(w + pl.part_bytes, kAlign);
   pl.ws_partml = w;
   w = align_up(w + segs * 4 * 64 * 2 * 4, kAlign);
   pl.ws_sync = w;
   w = align_up(w + units * rkv::kSyncStride * 8, kAlign);
-  // prepared queries: two e4m3 terms per element and an exponent per row and term
+  // prepared queries: up to three e4m3 terms per element and an exponent per row and term
   pl.ws.nq_pad = (int32_t)(nqg * 128);
   pl.ws_qcodes = w;
-  w = align_up(w + 2 * (size_t)H * pl.ws.nq_pad * D, kAlign);
+  w = align_up(w + 3 * (size_t)H * pl.ws.nq_pad * D, kAlign);
   pl.ws_qexp = w;
-  w = align_up(w + 2 * (size_t)H * pl.ws.nq_pad * 4, kAlign);
+  w = align_up(w + 3 * (size_t)H * pl.ws.nq_pad * 4, kAlign);
   pl.total = w;
   return pl;
 }
@@ -163,7 +171,12 @@ size_t ring_cache_bytes(const rkv_params* p) {
     g_err = why;
     return 0;
   }
-  return make_plan(p).total;
+  const Plan pl = make_plan(p);
+  if (pl.part_bytes >= kMaxPartBytes) {
+    g_err = "n_heads x max_queries too large for the attention workspace (partials must stay below 1 GiB)";
+    return 0;
+  }
+  return pl.total;
 }
 
 int ring_cache_create(const rkv_params* p, void* dev_buf, size_t bytes, hipStream_t stream,
@@ -176,6 +189,8 @@ int ring_cache_create(const rkv_params* p, void* dev_buf, size_t bytes, hipStrea
   if (reinterpret_cast<uintptr_t>(dev_buf) % kAlign)
     return fail(RKV_EINVAL, "dev_buf must be 256-byte aligned");
   const Plan pl = make_plan(p);
+  if (pl.part_bytes >= kMaxPartBytes)
+    return fail(RKV_EINVAL, "n_heads x max_queries too large for the attention workspace (partials must stay below 1 GiB)");
   if (bytes < pl.total)
     return fail(RKV_EINVAL, "buffer too small: need " + std::to_string(pl.total) + " bytes");
 

@@ -19,11 +19,11 @@ struct AttnWs {
   // line: tiles arrived (low half) | output blocks committed to a merge
   // (high half); zeroed for the call's units by q_prep_kernel
   unsigned long long* sync;
-  uint8_t* qcodes; // [2 terms][H][nq_pad][D] e4m3 codes of the RoPE'd queries
-  int32_t* qexp;   // [2 terms][H][nq_pad] E8M0 code (127 + e) of the 2^e scale of each query row and term
+  uint8_t* qcodes; // [3 terms][H][nq_pad][D] e4m3 codes of the RoPE'd queries
+  int32_t* qexp;   // [3 terms][H][nq_pad] E8M0 code (127 + e) of the 2^e scale of each query row and term
   int32_t nq_pad;  // max_queries rounded up to 128
   int32_t grid;    // persistent workgroups
-  int32_t terms;   // 2 = precise, 1 = fast
+  int32_t terms;   // 2 = precise (3 query terms, 2 probability terms), 1 = fast (one each)
   int32_t wait_ticks;  // bound on a merge wait, in ticks of the 100 MHz real-time clock
 };
 

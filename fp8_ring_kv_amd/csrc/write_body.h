@@ -138,20 +138,27 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
     // fp32 RoPE results (a rounding away from the exact rotation already):
     // y * (1/s).  Values are raw bf16, whose quotients often sit next to e4m3
     // midpoints: the exact quotient code (vquot_row).
+    // Static scales (once calibrated): correctly rounded quotients,
+    // saturating at +-448.  A head calibrated at amax 0 has a zero static
+    // scale and keeps the per-(token, head) rule, keys and values separately.
+    const float stk = smode ? L.stat[h0 + hh] : 0.f;
+    const float stv = smode ? L.stat[H + h0 + hh] : 0.f;
     float sk, sv, rk;
     VQuot qv;
-    if (smode) {  // static scales: correctly rounded quotients, saturating at +-448
-      sk = L.stat[h0 + hh];
-      sv = L.stat[H + h0 + hh];
-      rk = recip_scale(sk);
+    if (stk > 0.f) {
+      sk = stk;
+    } else {
+      sk = div448(ak * g.margin);
+    }
+    rk = recip_scale(sk);
+    if (stv > 0.f) {
+      sv = stv;
       qv.s = sv;
       qv.r = recip_scale(sv);
       qv.f = 1.f;
     } else {
-      const float amk = ak * g.margin, amv = av * g.margin;
-      sk = div448(amk);
+      const float amv = av * g.margin;
       sv = div448(amv);
-      rk = recip_scale(sk);
       qv = vquot_row(amv, sv);
     }
     uint2 ck, cv;

@@ -114,7 +114,10 @@ typedef struct {
 typedef struct rkv_cache rkv_cache; /* opaque host-side handle */
 
 /* Size in bytes of the cache buffer for these parameters (all layers, their
- * state, and the attention workspace), or 0 if the parameters are invalid. */
+ * state, and the attention workspace), or 0 if the parameters are invalid
+ * (including n_heads x max_queries so large that the attention's split-unit
+ * partials, (n_heads * ceil(max_queries / 128) + workgroups) * 256 * head_dim
+ * bytes, would reach 1 GiB). */
 size_t ring_cache_bytes(const rkv_params* p);
 
 /* Create a handle over a caller-owned device buffer of at least
@@ -211,8 +214,12 @@ int ring_cache_set_qk_norm(rkv_cache* c, int32_t layer, const void* wq_bf16, con
  * s = fp32(margin * amax / 448) (amax and the product in double precision).
  * From then on, every write of the layer quantizes with these scales
  * (e4m3 of the correctly rounded y / s, saturating) and stores them as the
- * slots' scales, and every delta rotation keeps each key's scale and clamps;
- * the attention is unchanged.  ring_cache_reset returns the layer to
+ * slots' scales, and every delta rotation requantizes each valid key with
+ * its head's static key scale and clamps (keys written before the
+ * calibration move from their per-token scale to the head's).  A head whose
+ * amax is 0 (nothing valid, or all zero) gets scale 0 and keeps the
+ * per-(token, head) rule for its keys (values).  The attention reads the
+ * slots' scales as before.  ring_cache_reset returns the layer to
  * per-(token, head) scales.  The mode is device state (graph-capturable).
  * margin in (0, 64] (the pages use 1.5).  Errors: RKV_EINVAL for a null
  * cache, a layer out of range or a bad margin; RKV_EHIP if the launch fails. */

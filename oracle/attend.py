@@ -29,20 +29,23 @@ The device kernel's declared numerics, which ``attend_method`` and
   scale 2**e with e the smallest integer such that amax(q) <= 448 * 2**e;
   codes = e4m3(q / 2**e).
   (A power of two is applied exactly inside the FP8 matrix instruction.)
-  With two terms (the default, "precise" mode) the residual
-  r = q - decode(codes) * 2**e is quantized the same way and the kernel
-  multiplies K by both terms; Q is then known to about 2**-8 relative.
+  With three terms (the default, "precise" mode) the residual
+  r = q - decode(codes) * 2**e is quantized the same way, and its residual
+  again, and the kernel multiplies K by all three; Q is then known to about
+  2**-12 relative.  (Two terms, about 2**-8, are not enough: where a query's
+  outlier channels meet a key's, the score error moved single outputs by up
+  to 2.9e-2 of the value scale.)
 * P.V in FP8: with P = 2**(S - m) (m the row maximum), the kernel feeds
   x = P * s_v[j] * c with c = 448 * 2**-headroom / vmax_h, vmax_h the largest
   value scale written to the head since the last reset (an upper bound of
   every cached s_v), as hi = e4m3(x) and, with two terms, as
   lo = e4m3(16 (x - hi)) / 16; it multiplies them by the V codes and divides
   by c * sum_j P.  The kernel keeps a running row maximum that it raises only
-  when a tile exceeds it by more than 2 in log2 units, so its P may reach 4:
-  headroom 2 keeps x <= 448.  ``attend_emul`` uses the final row maximum; the
-  kernel's running maximum changes which way some codes round, which the
+  when a tile exceeds it by more than 6 in log2 units, so its P may reach
+  64: headroom 6 keeps x <= 448.  ``attend_emul`` uses the final row maximum;
+  the kernel's running maximum changes which way some codes round, which the
   tolerance covers.
-* The single-term ("fast") mode drops both residual terms.
+* The single-term ("fast") mode uses one term for Q and one for P.
 """
 from __future__ import annotations
 
@@ -137,7 +140,7 @@ def p_terms_value(x: np.ndarray, terms: int) -> np.ndarray:
     return hi + lo
 
 
-def attend_method(st: RingState, q: np.ndarray, q_pos: np.ndarray, q_terms: int = 2) -> np.ndarray:
+def attend_method(st: RingState, q: np.ndarray, q_pos: np.ndarray, q_terms: int = 3) -> np.ndarray:
     """A-method: Q quantized with the kernel's rule, exact probabilities."""
     qr, slots = _prepare(st, q, q_pos)
     out = np.zeros(qr.shape, dtype=np.float64)
@@ -151,8 +154,8 @@ def attend_method(st: RingState, q: np.ndarray, q_pos: np.ndarray, q_terms: int 
     return out
 
 
-def attend_emul(st: RingState, q: np.ndarray, q_pos: np.ndarray, q_terms: int = 2,
-                p_terms: int = 2, headroom: int = 2) -> np.ndarray:
+def attend_emul(st: RingState, q: np.ndarray, q_pos: np.ndarray, q_terms: int = 3,
+                p_terms: int = 2, headroom: int = 6) -> np.ndarray:
     """A-emul: A-method plus the FP8 rounding of P' = P * s_v[j] * c (see module doc)."""
     qr, slots = _prepare(st, q, q_pos)
     out = np.zeros(qr.shape, dtype=np.float64)

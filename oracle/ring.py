@@ -26,8 +26,15 @@ statement:
 * the pages' own scale mode (§4.3, Appendix G) is available after
   ``calibrate_static``: per-head scales from the amax of the dequantized
   cache over the valid slots times a margin, saturating writes with them,
-  and reset rotations that keep each key's scale and clamp; ``reset``
-  returns to per-(token, head) scales.
+  and reset rotations that requantize every valid key of the head with the
+  head's scale and clamp (keys written after the calibration already carry
+  it; older keys, quantized with their own per-token scale, move to it --
+  the head's scale covers any rotation of them, since a rotated pair's
+  component is at most the pair's norm, at most sqrt(2) times the head's
+  amax, below the margin of 1.5 the pages use); a head whose amax was 0 at
+  calibration keeps per-(token, head) scales (a zero scale would store zero
+  codes for every later write); ``reset`` returns to per-(token, head)
+  scales.
 
 State layout (canonical, independent of any device layout): codes [H][N][D]
 uint8, scales [H][N] float64 holding fp32 values, slot_pos [N] int64, and
@@ -120,8 +127,8 @@ def write(st: RingState, k: np.ndarray, v: np.ndarray, pos: np.ndarray) -> None:
         ck, sk = e4m3.quantize_rows(k_rot, st.margin)  # [n, H, D], [n, H]
         cv, sv = e4m3.quantize_rows(v, st.margin)
     else:
-        ck, sk = quantize_static(k_rot, st.static_k)
-        cv, sv = quantize_static(v, st.static_v)
+        ck, sk = quantize_static(k_rot, st.static_k, st.margin)
+        cv, sv = quantize_static(v, st.static_v, st.margin)
     slots = write_slots(st, n)
     st.codes_k[:, slots, :] = np.transpose(ck, (1, 0, 2))
     st.codes_v[:, slots, :] = np.transpose(cv, (1, 0, 2))
@@ -146,11 +153,14 @@ def rotate(st: RingState, delta: int) -> None:
     c, s = delta_angles(st.head_dim, delta, st.rope_base)
     x = e4m3.decode(st.codes_k[:, slots, :]) * st.scale_k[:, slots][..., None]
     y = rotate_pairs(x, c, s)
-    if st.static_k is None:
-        ck, sk = e4m3.quantize_rows(y, st.margin)
-    else:  # the pages' own mode: the same scale, values beyond it saturate
-        sk = st.scale_k[:, slots]
-        ck = e4m3.encode(y / np.where(sk > 0, sk, 1.0)[..., None])
+    ck, sk = e4m3.quantize_rows(y, st.margin)
+    if st.static_k is not None:
+        # the pages' own mode: requantize with the head's scale, values beyond
+        # it saturate; heads calibrated at amax 0 stay per-(token, head)
+        for h in np.flatnonzero(st.static_k > 0):
+            sh = st.static_k[h]
+            ck[h] = e4m3.encode(y[h] / sh)
+            sk[h] = sh
     st.codes_k[:, slots, :] = ck
     st.scale_k[:, slots] = sk
     st.slot_pos[slots] = st.slot_pos[slots] + delta
@@ -166,21 +176,25 @@ def reset(st: RingState) -> None:
     st.static_k = st.static_v = None
 
 
-def quantize_static(y: np.ndarray, s_head: np.ndarray):
+def quantize_static(y: np.ndarray, s_head: np.ndarray, margin: float):
     """Codes of [n, H, D] rows with one fixed scale per head: e4m3(y / s_h),
-    saturating at +-448 (values beyond the scale clip); scale 0 gives codes 0.
+    saturating at +-448 (values beyond the scale clip).  A head whose static
+    scale is 0 (amax 0 at calibration) keeps the per-(token, head) rule.
     Returns (codes, per-row scales [n, H])."""
-    s = np.broadcast_to(np.asarray(s_head, dtype=np.float64)[None, :], y.shape[:2])
-    safe = np.where(s > 0, s, 1.0)
-    codes = e4m3.encode(np.where(s[..., None] > 0, y / safe[..., None], 0.0))
-    return codes, np.array(s)
+    codes, s = e4m3.quantize_rows(y, margin)
+    for h in np.flatnonzero(np.asarray(s_head) > 0):
+        codes[:, h] = e4m3.encode(y[:, h] / s_head[h])
+        s[:, h] = s_head[h]
+    return codes, s
 
 
 def calibrate_static(st: RingState, margin: float) -> None:
     """The pages' scale calibration (Appendix G; §4.3 "FP8 at write"): per
     head, s = fp32(margin * amax / 448) with amax the largest magnitude of the
     dequantized keys (values) over the valid slots, then every later write
-    quantizes with these scales and a reset rotation keeps them."""
+    quantizes with these scales and a reset rotation requantizes the head's
+    keys with its key scale.  A scale of 0 (amax 0: no valid slot, or all
+    zero) leaves that head's keys (values) on per-(token, head) scales."""
     slots = valid_slots(st)
     amk = np.zeros(st.n_heads)
     amv = np.zeros(st.n_heads)

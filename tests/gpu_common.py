@@ -66,6 +66,54 @@ def pair_ulp_bound(codes, scale):
     return np.repeat(pn, 2, axis=-1) * scale[..., None]
 
 
+def state_from_device(cache: rkv.RingCache, layer: int):
+    """The device cache of `layer` as an oracle RingState (codes, scales,
+    positions, ring state, value-scale bound and, once calibrated, the static
+    scales), so an oracle operation can start from exactly what the device
+    holds."""
+    from oracle import ring as oring
+    (head, nv), sp, ck, cv, sk, sv = readback(cache, layer)
+    st = oring.RingState(cache.n_slots, cache.n_heads, cache.head_dim, rope_base=cache.params.rope_base,
+                         margin=cache.params.scale_margin, head=head, n_valid=nv,
+                         slot_pos=sp.copy(), codes_k=ck.copy(), codes_v=cv.copy(), scale_k=sk.copy(),
+                         scale_v=sv.copy(), vmax=cache.vmax(layer).cpu().numpy().astype(np.float64))
+    if cache.static_flag(layer):
+        stat = cache.static_scales(layer).cpu().numpy().astype(np.float64)
+        st.static_k, st.static_v = stat[0].copy(), stat[1].copy()
+    return st
+
+
+def check_rotated(cache: rkv.RingCache, layer: int, pre, delta: int):
+    """After a delta rotation of `layer` on the device: the oracle rotates
+    `pre` (the device's own state before the rotation, from
+    state_from_device), and every valid dequantized key of the device must be
+    within 1 e4m3 ulp of the oracle's (no exceptions), slot positions and
+    ring state bit-exact, values and value scales untouched.  Returns the
+    oracle's rotated state."""
+    from oracle import ring as oring
+    want = pre.copy()
+    oring.rotate(want, delta)
+    (head, nv), sp, ck, cv, sk, sv = readback(cache, layer)
+    assert (head, nv) == (want.head, want.n_valid), (layer, head, nv)
+    assert np.array_equal(sp, want.slot_pos), f"layer {layer}: slot positions"
+    assert np.array_equal(cv, pre.codes_v) and np.array_equal(sv, pre.scale_v), f"layer {layer}: values touched"
+    valid = oring.valid_slots(want)
+    bad, worst = within_one_ulp(ck[:, valid], sk[:, valid], want.codes_k[:, valid], want.scale_k[:, valid])
+    assert not bad.any(), (f"layer {layer}: {int(bad.sum())} of {bad.size} rotated key elements beyond 1 e4m3 ulp "
+                           f"of the oracle's rotation of the device's own keys (worst ratio {worst:.3f})")
+    return want
+
+
+def rotate_checked(cache: rkv.RingCache, layer: int, delta: int):
+    """Delta rotation of `layer` (-1: every layer) on the device, checked in
+    isolation against the oracle's rotation of the device's own pre-rotation
+    state (check_rotated).  Returns the oracle states it compared against."""
+    layers = range(cache.n_layers) if layer == -1 else [layer]
+    pres = [state_from_device(cache, l) for l in layers]
+    cache.rotate(layer, delta)
+    return [check_rotated(cache, l, pre, delta) for l, pre in zip(layers, pres)]
+
+
 def assert_cache_matches(cache, layer, st, slots=None, check_v=True, pre=None):
     """Bit-exact head/n_valid/slot_pos; K (and V) within 1 ulp on valid slots.
 
@@ -98,6 +146,20 @@ def assert_cache_matches(cache, layer, st, slots=None, check_v=True, pre=None):
                 v_codes_equal=float(np.mean(cv[:, valid] == st.codes_v[:, valid])))
 
 
+def gate(name, gpu, ref, sigma, max_tol=2e-2, mean_tol=2e-3, raw=False, quiet=False):
+    """Attention gate: the error divided by max(1, sigma_v) within max_tol /
+    mean_tol (and the raw error too when `raw`); raw and normalized errors
+    are printed and carried in the assertion message either way."""
+    rmax, rmean, nmax, nmean = attn_errors(gpu, ref, sigma)
+    msg = f"{name}: raw max {rmax:.2e} mean {rmean:.2e} | normalized max {nmax:.2e} mean {nmean:.2e}"
+    if not quiet:
+        print(msg, flush=True)
+    assert nmax < max_tol and nmean < mean_tol, msg
+    if raw:
+        assert rmax < max_tol and rmean < mean_tol, msg + " (raw gate)"
+    return rmax, rmean, nmax, nmean
+
+
 def attn_errors(gpu: np.ndarray, ref: np.ndarray, sigma: np.ndarray):
     """(raw max, raw mean, normalized max, normalized mean) of |gpu - ref|.
 
@@ -107,3 +169,49 @@ def attn_errors(gpu: np.ndarray, ref: np.ndarray, sigma: np.ndarray):
     e = np.abs(gpu - ref)
     en = e / np.maximum(1.0, sigma)[None]
     return float(e.max()), float(e.mean()), float(en.max()), float(en.mean())
+
+
+def check_attention(name, cache, layer, st, q, q_pos, out, raw=False, fast=False, ds=None, quiet=False):
+    """The attention gates of one call.
+
+    1. Primary: the device output against exact float64 attention over the
+       device's own dequantized cache (state_from_device): errors divided by
+       max(1, sigma_v) within 2e-2 max / 2e-3 mean, raw too when `raw`.  (Fast
+       mode is gated here only when `raw`: its single-term numerics miss the
+       bounds on outlier caches; it is held to its emulation below.)
+    2. The kernel's declared numerics (attend_emul: three query terms and two
+       probability terms, or one of each in fast mode) on the same cache, same
+       bounds.
+    3. End to end against the oracle's own session `st`: every cached element
+       may differ from the device's by 1 e4m3 ulp, which moves exact attention
+       itself (a near-tie key code in an outlier channel that rounds the other
+       way changes a dominant score); the device output may differ from the
+       oracle's exact attention by that movement plus the 2e-2 / 2e-3 bounds,
+       element by element.
+    `ds`: the device state when the caller already read it back.  Returns the
+    error tuples (device-state exact, end-to-end)."""
+    from oracle import attend as oatt
+    from oracle.bf16 import round_bf16
+    if ds is None:
+        ds = state_from_device(cache, layer)
+    sig = oatt.sigma_v(ds)
+    ex_d = oatt.attend_exact(ds, q, q_pos)
+    prim = None
+    if not fast or raw:
+        prim = gate(f"{name} vs exact on the device cache", out, ex_d, sig, raw=raw, quiet=quiet)
+    qt, pt = (1, 1) if fast else (3, 2)
+    gate(f"{name} vs emul(q {qt}, p {pt}) on the device cache", out,
+         round_bf16(oatt.attend_emul(ds, q, q_pos, qt, pt)), sig, quiet=quiet)
+    if st is None:
+        return prim, None
+    ex_o = oatt.attend_exact(st, q, q_pos)
+    norm = np.maximum(1.0, sig)[None]
+    e2e = np.abs(out - ex_o) / norm
+    move = np.abs(ex_d - ex_o) / norm
+    msg = (f"{name} end to end vs the oracle's session: normalized max {e2e.max():.2e} mean {e2e.mean():.2e}; "
+           f"exact attention moved by the cache's 1-ulp differences: max {move.max():.2e} mean {move.mean():.2e}")
+    if not quiet:
+        print(msg, flush=True)
+    if not fast or raw:
+        assert np.all(e2e <= move + 2e-2) and e2e.mean() <= move.mean() + 2e-3, msg
+    return prim, (float(e2e.max()), float(e2e.mean()))

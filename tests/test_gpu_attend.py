@@ -1,19 +1,28 @@
 """GPU parity of cache_attend against the oracle.
 
 Gates (the hot path's float contract, max-abs 2e-2 / mean-abs 2e-3 on bf16
-outputs against an fp64 oracle on the dequantized cache):
+outputs against an fp64 oracle on the dequantized cache), per call
+(gpu_common.check_attention):
 
-* precise mode (two-term Q and P, the default) vs ``attend_exact``: errors
-  divided by max(1, sigma_v[head, channel]) within 2e-2 max / 2e-3 mean on
-  every workload; raw errors within the same bounds on N(0,1) workloads
-  (where sigma_v ~ 1 the two coincide);
-* precise mode vs ``attend_emul`` (its declared numerics): same bounds;
+* precise mode (three-term Q, two-term P: the default) vs exact float64 attention
+  over the dequantized cache the kernel read (the device's own cache,
+  every element of which is checked within 1 e4m3 ulp of the oracle's in
+  test_gpu_cache): errors divided by max(1, sigma_v[head, channel]) within
+  2e-2 max / 2e-3 mean on every workload, and raw errors within the same
+  bounds on N(0,1) workloads (where sigma_v ~ 1 the two coincide);
+* the kernel's declared numerics (``attend_emul``) on the same cache, same
+  bounds;
+* end to end against the oracle's own session: within the bounds plus the
+  amount by which exact attention itself moves between the two caches' 1-ulp
+  differences (on the stress workload one key code of an outlier channel
+  that rounds the other way moves head 6's output by 0.13);
 * fast mode (single-term) vs ``attend_emul(q_terms=1, p_terms=1)`` and, on
-  N(0,1) data, raw vs ``attend_exact``.
+  N(0,1) data, raw vs exact.
 
-The outputs of bf16 rounding alone reach the raw bound on channels whose
-values are ~8x larger (outlier channels), which is why errors are
-normalized per output channel.
+Full-size workloads compare every output element (all heads, all query
+rows).  Raw errors are printed and carried in every assertion message; on
+outlier workloads the raw gate is not applied, because bf16 rounding alone of
+outputs ~10-20 exceeds it on channels whose values are ~8x larger.
 """
 import numpy as np
 import pytest
@@ -22,7 +31,7 @@ import torch
 import fp8_ring_kv_amd as rkv
 from oracle import attend as oatt, ring as oring
 from oracle.bf16 import round_bf16
-from tests.gpu_common import DEV, attn_errors, pos_dev, require_gpu, to_dev
+from tests.gpu_common import DEV, attn_errors, check_attention, gate, pos_dev, require_gpu, to_dev
 from workloads import ATTEND, STRESS, TINY, Bf16, Config, OutlierSpec, Stream, positions
 
 pytestmark = pytest.mark.gpu
@@ -31,15 +40,6 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     require_gpu()
-
-
-def gate(name, gpu, ref, sigma, max_tol=2e-2, mean_tol=2e-3, raw=False):
-    rmax, rmean, nmax, nmean = attn_errors(gpu, ref, sigma)
-    print(f"{name}: raw max {rmax:.2e} mean {rmean:.2e} | norm max {nmax:.2e} mean {nmean:.2e}")
-    assert nmax < max_tol and nmean < mean_tol, name
-    if raw:
-        assert rmax < max_tol and rmean < mean_tol, name + " (raw)"
-    return rmax, rmean, nmax, nmean
 
 
 def sub_heads(x: Bf16, heads) -> Bf16:
@@ -61,7 +61,8 @@ def test_tiny_session(precision):
     cache = rkv.RingCache(1, cfg.n_slots, 1, 64, 16, precision, device=DEV)
     st = oring.RingState(cfg.n_slots, 1, 64)
     s = Stream(cfg)
-    terms = 2 if precision == rkv.RKV_PRECISE else 1
+    fast = precision == rkv.RKV_FAST
+    terms = 1 if fast else 2
     chunks = []
     for c in range(6):
         q, k, v = s.chunk()
@@ -70,17 +71,12 @@ def test_tiny_session(precision):
         oring.write(st, k.f64, v.f64, pos)
         chunks.append((q, pos))
         out = gpu_out(cache.attend(0, to_dev(q), pos_dev(pos)))
-        sig = oatt.sigma_v(st)
-        emul = round_bf16(oatt.attend_emul(st, q.f64, pos, terms, terms))
-        gate(f"tiny[{c}] vs emul", out, emul, sig)
-        if precision == rkv.RKV_PRECISE:
-            gate(f"tiny[{c}] vs exact", out, oatt.attend_exact(st, q.f64, pos), sig, raw=True)
+        check_attention(f"tiny[{c}]", cache, 0, st, q.f64, pos, out, raw=not fast, fast=fast)
     cache.rotate(0, -80)
     oring.rotate(st, -80)
     q, pos = chunks[5]
     out = gpu_out(cache.attend(0, to_dev(q), pos_dev(pos - 80)))
-    emul = round_bf16(oatt.attend_emul(st, q.f64, pos - 80, terms, terms))
-    gate("tiny after reset vs emul", out, emul, oatt.sigma_v(st))
+    check_attention("tiny after reset", cache, 0, st, q.f64, pos - 80, out, raw=not fast, fast=fast)
 
 
 def build_attend_cache(cfg, heads_checked, precision=rkv.RKV_PRECISE, total=8888, max_q=757):
@@ -100,12 +96,12 @@ def build_attend_cache(cfg, heads_checked, precision=rkv.RKV_PRECISE, total=8888
     return cache, st, s
 
 
-def test_attend_workload_full_size_sampled():
-    """757 queries x 5,788 slots x 12 heads, ring head at slot 3,100, 2% outliers x8.
-
-    The GPU computes every output; the oracle checks 3 heads on 160 sampled rows."""
+def test_attend_workload_full_size():
+    """757 queries x 5,788 slots x 12 heads, ring head at slot 3,100, 2% outliers x8,
+    in the launch configuration the benchmark times: every output element is
+    compared with the oracle."""
     cfg = ATTEND
-    heads = [0, 5, 11]
+    heads = list(range(cfg.n_heads))
     cache, st, s = build_attend_cache(cfg, heads)
     torch.cuda.synchronize()
     assert int(cache.state(0)[0]) == 3100 and int(cache.state(0)[1]) == 5788
@@ -113,15 +109,8 @@ def test_attend_workload_full_size_sampled():
     q, _, _ = s.chunk(757)
     qpos = positions(8131, 757)
     out = gpu_out(cache.attend(0, to_dev(q), pos_dev(qpos)))
-    rows = np.unique(np.concatenate([np.arange(0, 757, 5), [756, 755, 31, 32, 33]]))
-    qs = sub_heads(Bf16(q.bits[rows], q.f64[rows]), heads)
-    sig = oatt.sigma_v(st)
-    ex = oatt.attend_exact(st, qs.f64, qpos[rows])
-    em = round_bf16(oatt.attend_emul(st, qs.f64, qpos[rows]))
-    g = out[rows][:, heads]
-    gate("C2 vs exact (normalized)", g, ex, sig)
-    gate("C2 vs emul", g, em, sig)
     assert np.all(np.isfinite(out))
+    check_attention("C2 (all 12 heads x 757 rows)", cache, 0, st, q.f64, qpos, out)
 
 
 def test_attend_fast_mode_on_unit_normal_data():
@@ -131,9 +120,7 @@ def test_attend_fast_mode_on_unit_normal_data():
     q, _, _ = s.chunk(200)
     qpos = positions(5800, 200)
     out = gpu_out(cache.attend(0, to_dev(q), pos_dev(qpos)))
-    sig = oatt.sigma_v(st)
-    gate("fast vs exact raw (N(0,1))", out, oatt.attend_exact(st, q.f64, qpos), sig, raw=True)
-    gate("fast vs emul(1,1)", out, round_bf16(oatt.attend_emul(st, q.f64, qpos, 1, 1)), sig)
+    check_attention("fast mode, N(0,1)", cache, 0, st, q.f64, qpos, out, raw=True, fast=True)
 
 
 def test_empty_cache_gives_zeros():
@@ -172,8 +159,7 @@ def test_partial_fill_masks_invalid_slots():
     q, _, _ = s.chunk(100)
     qpos = positions(700, 100)
     out = gpu_out(cache.attend(0, to_dev(q), pos_dev(qpos)))
-    sig = oatt.sigma_v(st)
-    gate("partial vs exact", out, oatt.attend_exact(st, q.f64, qpos), sig)
+    check_attention("partial fill", cache, 0, st, q.f64, qpos, out)
 
 
 def test_wrapped_ring_equals_linear_cache():
@@ -201,13 +187,14 @@ def test_wrapped_ring_equals_linear_cache():
 
 
 def test_stress_partial_fill_sessions():
-    """48 heads x 11,576 slots, 1% outliers x16, attends while the ring fills, one reset."""
+    """48 heads x 11,576 slots, 1% outliers x16, attends while the ring fills
+    (valid 757, 1,514, ..., full at write 16), one reset after write 21; every
+    output element of every checked attention is compared with the oracle."""
     cfg = STRESS
-    heads = [3, 47]
+    heads = list(range(cfg.n_heads))
     cache = rkv.RingCache(1, cfg.n_slots, cfg.n_heads, 128, 757, device=DEV)
     st = oracle_state(cfg, heads)
     s = Stream(cfg)
-    rows = np.arange(0, 757, 11)
     for w in range(24):
         q, k, v = s.chunk()
         pos = positions(757 * w, 757)
@@ -217,12 +204,11 @@ def test_stress_partial_fill_sessions():
             oring.rotate(st, d)
         p = pos - (21 * 757 if w >= 21 else 0)
         cache.write(0, to_dev(k), to_dev(v), pos_dev(p))
-        oring.write(st, sub_heads(k, heads).f64, sub_heads(v, heads).f64, p)
+        oring.write(st, k.f64, v.f64, p)
         if w in (0, 1, 7, 15, 16, 21, 23):
             out = gpu_out(cache.attend(0, to_dev(q), pos_dev(p)))
-            qs = sub_heads(Bf16(q.bits[rows], q.f64[rows]), heads)
-            ex = oatt.attend_exact(st, qs.f64, p[rows])
-            gate(f"stress write {w} (valid {st.n_valid})", out[rows][:, heads], ex, oatt.sigma_v(st))
+            check_attention(f"stress write {w} (valid {st.n_valid}), all 48 heads x 757 rows", cache, 0, st,
+                            q.f64, p, out)
 
 
 @pytest.mark.parametrize("n_slots,n_heads,n_q,workgroups", [
@@ -258,8 +244,7 @@ def test_merge_schedule_leaves_results_unchanged(n_slots, n_heads, n_q, workgrou
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
-    gate(f"merge schedule ({workgroups} workgroups)", gpu_out(outs[0]),
-         oatt.attend_exact(st, q.f64, qpos), oatt.sigma_v(st))
+    check_attention(f"merge schedule ({workgroups} workgroups)", caches[0], 0, st, q.f64, qpos, gpu_out(outs[0]))
 
 
 def test_attend_rejects_bad_arguments():

@@ -3,6 +3,12 @@
 Contract (Runway Characters paper §4.1-§4.3, Appendix G, stated as a bar):
 ring head, n_valid and every slot position bit-exact; every dequantized
 K and V element within 1 e4m3 ulp of the oracle's.
+
+Every rotation is checked twice: in isolation (rotate_checked: the oracle
+rotates the device's own pre-rotation keys, and every rotated key element
+must be within 1 ulp, with no exceptions), and end to end against the
+oracle's own session, where the write's 1-ulp difference before the
+rotation is carried through it.
 """
 import numpy as np
 import pytest
@@ -10,7 +16,7 @@ import torch
 
 import fp8_ring_kv_amd as rkv
 from oracle import e4m3, ring as oring
-from tests.gpu_common import DEV, assert_cache_matches, pos_dev, readback, require_gpu, to_dev
+from tests.gpu_common import DEV, assert_cache_matches, pos_dev, readback, require_gpu, rotate_checked, to_dev
 from workloads import TINY, WRITE_ROTATE, Bf16, Config, OutlierSpec, Stream, f32_to_bf16_bits, bf16_bits_to_f64, positions
 
 pytestmark = pytest.mark.gpu
@@ -39,7 +45,7 @@ def test_tiny_session_writes_then_reset():
         assert_cache_matches(cache, 0, st)
     assert (st.head, st.n_valid) == (32, 64)
     pre = st.copy()
-    cache.rotate(0, -80)
+    rotate_checked(cache, 0, -80)
     oring.rotate(st, -80)
     assert_cache_matches(cache, 0, st, pre=pre)
 
@@ -133,7 +139,7 @@ def test_wrapping_writes_of_varied_sizes(head_dim):
         oring.write(st, k.f64, v.f64, pos)
         assert_cache_matches(cache, 0, st)
     pre = st.copy()
-    cache.rotate(0, -1234)
+    rotate_checked(cache, 0, -1234)
     oring.rotate(st, -1234)
     assert_cache_matches(cache, 0, st, pre=pre)
 
@@ -148,7 +154,7 @@ def test_partial_fill_rotate_touches_valid_slots_only():
     oring.write(st, k.f64, v.f64, pos)
     before = readback(cache, 0)
     pre = st.copy()
-    cache.rotate(0, 77)
+    rotate_checked(cache, 0, 77)
     oring.rotate(st, 77)
     assert_cache_matches(cache, 0, st, pre=pre)
     after = readback(cache, 0)
@@ -180,7 +186,7 @@ def test_write_rotate_workload_full_size():
             assert_cache_matches(cache, 0, st)
     d = -42 * 757
     pre = st.copy()
-    cache.rotate(0, d)
+    rotate_checked(cache, 0, d)
     oring.rotate(st, d)
     stats = assert_cache_matches(cache, 0, st, pre=pre)
     print("codes equal to the oracle's:", stats)
@@ -200,7 +206,7 @@ def test_rotate_all_layers_in_one_launch():
         cache.write(layer, to_dev(k), to_dev(v), pos_dev(pos))
         oring.write(st, k.f64, v.f64, pos)
         states.append(st)
-    cache.rotate(-1, -9)
+    rotate_checked(cache, -1, -9)
     for layer, st in enumerate(states):
         pre = st.copy()
         oring.rotate(st, -9)

@@ -97,7 +97,7 @@ def test_one_valid_slot_returns_its_value():
         out = fn(st, q, np.arange(7))
         assert np.max(np.abs(out - vd[None])) < 1e-15, fn.__name__
     # emul: P' = 1 * s_v * c = 448 * 2**-headroom exactly up to the fp32 rounding of c
-    for hr in (0, 2):
+    for hr in (0, 2, 6):
         out = attend.attend_emul(st, q, np.arange(7), headroom=hr)
         assert np.all(np.abs(out - vd[None]) <= 2 ** -22 * np.abs(vd[None]))
 
@@ -241,16 +241,51 @@ def test_sigma_v_shape_and_value():
     assert np.allclose(sv[0], np.sqrt((vd[0] ** 2).mean(axis=0)))
 
 
-def test_two_term_q_error_bound():
-    """Two power-of-two e4m3 terms carry Q to about 2**-8 of its amax."""
+def test_sigma_v_closed_form_on_partial_wrapped_ring():
+    """A hand-built 8-slot ring holding 3 valid slots that wrap (head 2,
+    n_valid 3: slots 7, 0, 1); every other slot holds huge values.  The codes
+    and scales make each dequantized value an exact small number, so the
+    per-(head, channel) RMS over the valid slots has a closed form: channel 0
+    holds 1, 2, 2 (sqrt 3), channel 1 holds -2, 2, 0 (sqrt(8/3)), channel 2
+    holds 0, 0, 0 (0), channel 3 holds 4, 4, 4 (4); head 1 is head 0 times 2.
+    Averaging over all slots, over N instead of n_valid, or over the slots
+    [0, n_valid) instead of the cyclic range gives other values."""
+    st = ring.RingState(8, 2, 4, head=2, n_valid=3)
+    one, two, four, mtwo, big = 0x38, 0x40, 0x48, 0xC0, 0x7E  # 1, 2, 4, -2, 448
+    st.codes_v[:] = big
+    st.scale_v[:] = 1000.0
+    rows = {7: [one, mtwo, 0, four], 0: [two, two, 0, four], 1: [two, 0, 0, four]}
+    for slot, codes in rows.items():
+        st.codes_v[:, slot] = codes
+        st.scale_v[0, slot] = 1.0
+        st.scale_v[1, slot] = 2.0
+    want = np.array([np.sqrt(3.0), np.sqrt(8.0 / 3.0), 0.0, 4.0])
+    sv = attend.sigma_v(st)
+    assert np.allclose(sv[0], want, rtol=0, atol=1e-15)
+    assert np.allclose(sv[1], 2 * want, rtol=0, atol=1e-15)
+    # the empty ring normalizes by 1
+    assert np.array_equal(attend.sigma_v(ring.RingState(8, 2, 4)), np.ones((2, 4)))
+
+def test_q_term_error_bounds():
+    """Power-of-two e4m3 terms: one carries Q to half an ulp of 448 over its
+    amax, two to about 2**-8 of it, three to about 2**-12; each term gains
+    about 4 bits (e4m3 holds 3 mantissa bits plus the rounding bit)."""
     rng = np.random.default_rng(12)
     q = rng.standard_normal((300, 3, 128)) * rng.uniform(0.01, 50, (300, 3, 1))
     amax = np.max(np.abs(q), axis=-1, keepdims=True)
     one = attend.quantize_q_terms(q, 1)
     two = attend.quantize_q_terms(q, 2)
+    three = attend.quantize_q_terms(q, 3)
     assert np.all(np.abs(one - q) <= amax * 16 / 224)  # half ulp at 448 over a 224..448 amax
     assert np.all(np.abs(two - q) <= amax / 224)
+    assert np.all(np.abs(three - q) <= amax / (224 * 16))
     assert np.max(np.abs(two - q) / amax) < np.max(np.abs(one - q) / amax) / 8
+    assert np.max(np.abs(three - q) / amax) < np.max(np.abs(two - q) / amax) / 8
+    # each element on its own: two terms within 2**-8 of its magnitude, three
+    # within 2**-12 (all these elements are far above the subnormal range)
+    big = np.abs(q) > amax * 2 ** -6
+    assert np.all(np.abs(two - q)[big] <= np.abs(q)[big] * 2 ** -8)
+    assert np.all(np.abs(three - q)[big] <= np.abs(q)[big] * 2 ** -12)
 
 
 def test_two_term_p_closed_forms_and_bound():
@@ -264,7 +299,7 @@ def test_two_term_p_closed_forms_and_bound():
 
 
 def test_declared_numerics_meet_contract_on_outlier_cache():
-    """Precise mode (two-term Q and P) vs exact: normalized 2e-2 max / 2e-3 mean.
+    """Precise mode (three-term Q, two-term P) vs exact: normalized 2e-2 max / 2e-3 mean.
 
     A full 5,788-slot cache written in 757-token chunks with 2% outlier
     channels x8, ring head at slot 3,100; 2 heads and 96 queries keep it fast.
@@ -325,8 +360,8 @@ def test_emul_exact_when_scaled_probabilities_are_representable():
     for terms in (1, 2):
         out = attend.attend_emul(st, q, np.arange(5), p_terms=terms)
         assert np.max(np.abs(out[:, 0, :] - mean_v[None])) <= 1e-14 * np.max(np.abs(mean_v)), terms
-    # a value scale above vmax would push P s_v c past 112 (the headroom) but
-    # still inside e4m3 for a factor of 4: the same closed form holds
+    # a value scale above vmax would push P s_v c past 448 * 2**-headroom but
+    # stays inside e4m3 for a factor of 4: the same closed form holds
     st.scale_v[0, 0] = big * 4.0
     mean_v = (e4m3.decode(st.codes_v[0]) * st.scale_v[0][:, None]).mean(axis=0)
     out = attend.attend_emul(st, q, np.arange(5))

@@ -68,3 +68,83 @@ def test_reset_returns_to_per_token_scales():
     ring.calibrate_static(st, 1.5)
     ring.reset(st)
     assert st.static_k is None and st.static_v is None
+
+
+def test_rotation_right_after_calibration_moves_old_keys_to_the_head_scale():
+    """Keys written with per-token scales before the calibration and rotated
+    before any rewrite: the rotation requantizes them with the head's static
+    scale, which covers every rotated component (pair norm <= sqrt(2) amax <
+    1.5 amax), so nothing clips and every key stays within the write's
+    rounding plus one requantization of RoPE at the shifted position."""
+    rng = np.random.default_rng(7)
+    st = ring.RingState(700, 2, 64)
+    ks, pos = [], []
+    for c in range(2):
+        k = rng.standard_normal((300, 2, 64))
+        p = np.arange(300 * c, 300 * c + 300)
+        ring.write(st, k, rng.standard_normal((300, 2, 64)), p)
+        ks.append(k)
+        pos.append(p)
+    ring.calibrate_static(st, 1.5)
+    per_token = st.scale_k.copy()
+    ring.rotate(st, -600)
+    slots = ring.valid_slots(st)  # the 600 keys in write order
+    assert np.all(st.scale_k[:, slots] == st.static_k[:, None])
+    assert np.max(np.abs(e4m3.decode(st.codes_k[:, slots]))) < 448  # nothing clipped
+    got = e4m3.decode(st.codes_k[:, slots, :]) * st.scale_k[:, slots][..., None]
+    want = np.transpose(rope(np.concatenate(ks), np.concatenate(pos) - 600), (1, 0, 2))
+    # write rounding: half a top-binade step of the per-token scale, carried
+    # through the rotation as a pair (sqrt 2); requantization: half a step of
+    # the static scale
+    bound = np.sqrt(2) * 16 * per_token[:, slots][..., None] + 16 * st.static_k[:, None, None]
+    assert np.all(np.abs(got - want) <= bound * (1 + 1e-9))
+    # keeping each key's own per-token scale instead would clip about half of them
+    kept = ring.RingState(700, 2, 64)
+    rng = np.random.default_rng(7)
+    for c in range(2):
+        ring.write(kept, rng.standard_normal((300, 2, 64)), rng.standard_normal((300, 2, 64)),
+                   np.arange(300 * c, 300 * c + 300))
+    x = e4m3.decode(kept.codes_k[:, slots]) * kept.scale_k[:, slots][..., None]
+    from oracle.rope import delta_angles, rotate_pairs
+    y = rotate_pairs(x, *delta_angles(64, -600))
+    clipped = np.any(np.abs(y) > 448 * kept.scale_k[:, slots][..., None], axis=-1)
+    assert clipped.mean() > 0.2
+
+
+def test_zero_amax_head_keeps_per_token_scales():
+    """Calibrating a layer with nothing valid (amax 0) gives zero static scales:
+    those heads keep the per-(token, head) rule, so later writes store the same
+    codes and scales as an uncalibrated ring instead of zero codes."""
+    rng = np.random.default_rng(8)
+    cal = ring.RingState(64, 2, 64)
+    ring.calibrate_static(cal, 1.5)
+    assert not cal.static_k.any() and not cal.static_v.any()
+    plain = ring.RingState(64, 2, 64)
+    k, v = rng.standard_normal((16, 2, 64)), rng.standard_normal((16, 2, 64))
+    for st in (cal, plain):
+        ring.write(st, k, v, np.arange(16))
+        ring.rotate(st, -5)
+    assert np.array_equal(cal.codes_k, plain.codes_k) and np.array_equal(cal.codes_v, plain.codes_v)
+    assert np.array_equal(cal.scale_k, plain.scale_k) and np.array_equal(cal.scale_v, plain.scale_v)
+    assert np.any(cal.codes_k[:, :16] != 0)
+
+
+def test_zero_key_head_static_values_only():
+    """A head whose cached keys are all zero but whose values are not: the keys
+    stay per-token (scale 0 static), the values go static."""
+    rng = np.random.default_rng(9)
+    st = ring.RingState(64, 2, 64)
+    k = rng.standard_normal((16, 2, 64))
+    k[:, 1] = 0.0
+    ring.write(st, k, rng.standard_normal((16, 2, 64)), np.arange(16))
+    ring.calibrate_static(st, 1.5)
+    assert st.static_k[1] == 0 and st.static_k[0] > 0 and np.all(st.static_v > 0)
+    k2 = rng.standard_normal((16, 2, 64))
+    v2 = rng.standard_normal((16, 2, 64))
+    ring.write(st, k2, v2, np.arange(16, 32))
+    new = np.arange(16, 32)
+    assert np.all(st.scale_k[0, new] == st.static_k[0])
+    assert np.all(st.scale_v[:, new] == st.static_v[:, None])
+    # head 1's keys: per-token rule, amax maps to 448
+    assert np.all(np.max(np.abs(e4m3.decode(st.codes_k[1, new])), axis=-1) == 448)
+    assert np.all(st.scale_k[1, new] == np.float32(np.max(np.abs(rope(k2, new)[:, 1]), axis=-1) / 448))
