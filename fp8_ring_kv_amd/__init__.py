@@ -22,7 +22,7 @@ __all__ = [
     "RKV_OK", "RKV_EINVAL", "RKV_EHIP", "RKV_PRECISE", "RKV_FAST",
     "rkv_params", "rkv_layout", "RkvError", "lib", "lib_path",
     "ring_cache_bytes", "ring_cache_create", "ring_cache_destroy", "ring_cache_reset",
-    "ring_cache_layout", "cache_write_rope_fp8", "cache_delta_rotate", "cache_attend",
+    "ring_cache_layout", "cache_write_rope_fp8", "cache_delta_rotate", "cache_attend", "cache_attend_noalloc",
     "cache_write_attend", "ring_cache_set_qk_norm", "ring_cache_calibrate_static",
     "rkv_last_error", "rkv_probe_fp8_mfma", "rkv_probe_stream", "RingCache",
 ]
@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
     L.cache_delta_rotate.restype = ctypes.c_int
     L.cache_attend.argtypes = [VP, I32, VP, VP, I32, VP, VP]
     L.cache_attend.restype = ctypes.c_int
+    L.cache_attend_noalloc.argtypes = [VP, I32, VP, VP, I32, VP, VP]
+    L.cache_attend_noalloc.restype = ctypes.c_int
     L.cache_write_attend.argtypes = [VP, I32, VP, VP, VP, I32, VP, VP, I32, VP, VP]
     L.cache_write_attend.restype = ctypes.c_int
     L.rkv_last_error.argtypes = []
@@ -172,6 +174,13 @@ def cache_attend(handle: int, layer: int, q: int, q_pos: int, n_q: int, out: int
                             n_q, ctypes.c_void_p(out), ctypes.c_void_p(stream))
     if rc != RKV_OK:
         raise RkvError(rc, "cache_attend")
+
+
+def cache_attend_noalloc(handle: int, layer: int, q: int, q_pos: int, n_q: int, out: int, stream: int) -> None:
+    rc = lib().cache_attend_noalloc(ctypes.c_void_p(handle), layer, ctypes.c_void_p(q), ctypes.c_void_p(q_pos),
+                                    n_q, ctypes.c_void_p(out), ctypes.c_void_p(stream))
+    if rc != RKV_OK:
+        raise RkvError(rc, "cache_attend_noalloc")
 
 
 def cache_write_attend(handle: int, layer: int, k: int, v: int, pos: int, n: int, q: int, q_pos: int,

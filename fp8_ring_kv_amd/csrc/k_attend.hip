@@ -49,11 +49,75 @@
 // moves only probabilities below about 1/100 of the row maximum into the
 // e4m3 subnormal range, where the second term still carries them.)
 #include <cmath>
+#include <mutex>
 
 #include "rkv_launch.h"
 #include "write_body.h"
 
 namespace rkv {
+
+// Fixed attention workspace of cache_attend_noalloc, for callers that cannot
+// allocate (graph capture, serving loops): one copy per device, held from
+// module load to process exit, shared by every such call on that device.
+// Host code never passes this name to a kernel (on the host it is only a
+// stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns, looked up once per device.
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t scratch_init() {
+  void* p = nullptr;
+  return scratch_ptr(&p);
+}
+
+hipError_t fixed_attn_ws(const Geom& g, const AttnWs& base, int n_q, AttnWs* out, size_t* need) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t H = g.n_heads, D = g.head_dim;
+  const size_t nq_pad = (size_t)(n_q + 127) / 128 * 128;
+  const size_t units = nq_pad / 128 * H;
+  const size_t segs = units + (size_t)base.grid;
+  const size_t o_part = 0;
+  const size_t o_ml = up(o_part + segs * 128 * D * 2);
+  const size_t o_sync = up(o_ml + segs * 4 * 64 * 2 * 4);
+  const size_t o_q = up(o_sync + units * kSyncStride * 8);
+  const size_t o_qe = up(o_q + 3 * H * nq_pad * D);
+  *need = up(o_qe + 3 * H * nq_pad * 4);
+  if (*need > kScratchBytes) return hipSuccess;
+  void* p = nullptr;
+  const hipError_t e = scratch_ptr(&p);
+  if (e != hipSuccess) return e;
+  uint8_t* b = static_cast<uint8_t*>(p);
+  *out = base;
+  out->part_o = b + o_part;
+  out->part_ml = reinterpret_cast<float*>(b + o_ml);
+  out->sync = reinterpret_cast<unsigned long long*>(b + o_sync);
+  out->qcodes = b + o_q;
+  out->qexp = reinterpret_cast<int32_t*>(b + o_qe);
+  out->nq_pad = (int32_t)nq_pad;
+  return hipSuccess;
+}
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));

@@ -217,6 +217,9 @@ int ring_cache_create(const rkv_params* p, void* dev_buf, size_t bytes, hipStrea
     delete c;
     return hip_fail(e, "fill kernel launch");
   }
+  // the fixed scratch of cache_attend_noalloc, looked up now on this device
+  // (a failure here is reported by that call, which tries again)
+  (void)rkv::scratch_init();
   e = rkv::launch_init_consts(c->g, c->half_turns, half, stream);
   if (e != hipSuccess) {
     delete c;
@@ -318,6 +321,29 @@ int cache_attend(rkv_cache* c, int32_t layer, const void* q_bf16, const int32_t*
     return fail(RKV_EINVAL, "n_q = " + std::to_string(n_q) + " outside [1, max_queries]");
   hipError_t e = rkv::launch_attend(c->g, c->ws, layer, q_bf16, q_pos, n_q, out_bf16, c->norm_q(layer),
                                      c->norm_eps[layer], stream);
+  if (e != hipSuccess) return hip_fail(e, "attend kernel launch");
+  return RKV_OK;
+}
+
+int cache_attend_noalloc(rkv_cache* c, int32_t layer, const void* q_bf16, const int32_t* q_pos,
+                         int32_t n_q, void* out_bf16, hipStream_t stream) {
+  if (!c) return fail(RKV_EINVAL, "cache is null");
+  int lo, hi;
+  if (int r = layer_range(c, layer, false, &lo, &hi)) return r;
+  if (!q_bf16 || !q_pos || !out_bf16) return fail(RKV_EINVAL, "null tensor pointer");
+  if (!aligned(q_bf16, 16) || !aligned(out_bf16, 16))
+    return fail(RKV_EINVAL, "q/out must be 16-byte aligned");
+  if (!aligned(q_pos, 4)) return fail(RKV_EINVAL, "q_pos must be 4-byte aligned");
+  if (n_q < 1 || n_q > c->p.max_queries)
+    return fail(RKV_EINVAL, "n_q = " + std::to_string(n_q) + " outside [1, max_queries]");
+  rkv::AttnWs ws;
+  size_t need = 0;
+  hipError_t e = rkv::fixed_attn_ws(c->g, c->ws, n_q, &ws, &need);
+  if (e != hipSuccess) return hip_fail(e, "scratch symbol lookup");
+  if (need > rkv::kScratchBytes)
+    return fail(RKV_EINVAL, "n_q x n_heads needs " + std::to_string(need) + " bytes of attention scratch, more than the " +
+                                std::to_string(rkv::kScratchBytes) + " bytes of the fixed scratch");
+  e = rkv::launch_attend(c->g, ws, layer, q_bf16, q_pos, n_q, out_bf16, c->norm_q(layer), c->norm_eps[layer], stream);
   if (e != hipSuccess) return hip_fail(e, "attend kernel launch");
   return RKV_OK;
 }

@@ -44,6 +44,17 @@ hipError_t launch_rotate(const Geom& g, int layer_lo, int layer_hi, int32_t delt
 hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void* q,
                          const int32_t* q_pos, int n_q, void* out, const uint16_t* wq, float eps,
                          hipStream_t s);
+// The attention workspace of one call of n_q queries placed in the library's
+// fixed device scratch (the entry point that allocates nothing): *need
+// receives its size in bytes; when it fits in kScratchBytes, *out is `base`
+// with its pointers moved into this device's scratch (the address found once
+// per device with hipGetSymbolAddress).  Returns the error of that lookup.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t fixed_attn_ws(const Geom& g, const AttnWs& base, int n_q, AttnWs* out, size_t* need);
+// Looks the scratch address up for the current device if not done yet (at
+// cache creation, so that a first cache_attend_noalloc under graph capture
+// finds it ready).
+hipError_t scratch_init();
 // Write, then attention, with the query preparation in the write's launch.
 hipError_t launch_write_attend(const Geom& g, const AttnWs& ws, int layer, const void* k, const void* v,
                                const int32_t* pos, int n, const void* q, const int32_t* q_pos, int n_q,

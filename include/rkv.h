@@ -171,6 +171,25 @@ int cache_delta_rotate(rkv_cache* c, int32_t layer, int32_t delta, hipStream_t s
 int cache_attend(rkv_cache* c, int32_t layer, const void* q_bf16, const int32_t* q_pos,
                  int32_t n_q, void* out_bf16, hipStream_t stream);
 
+/* cache_attend for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same attention, same arguments, results (bit for bit), requirements and
+ * errors, but the attention workspace (split-unit partials, arrival words,
+ * prepared queries) lives in a fixed 32 MiB scratch array inside the library
+ * (one per device, held from the library's load to process exit) instead of
+ * the cache buffer.  It calls no allocating routine.  The workspace of a call
+ * is (U + W) * (256 * D + 2048) + U * 128 * (3 * D + 13) bytes, U = H *
+ * ceil(n_q / 128) units and W the persistent workgroups (each area rounded
+ * up to 256 bytes); a call that would need more than 32 MiB returns
+ * RKV_EINVAL and enqueues nothing (12 heads x 757 queries at D = 128 with 512
+ * workgroups need about 23 MiB).  Every
+ * cache_attend_noalloc call on a device shares that device's scratch: calls
+ * that overlap on one device, from any cache or stream, race and must be
+ * ordered by the caller.  The scratch keeps the last call's contents; each
+ * call clears what must start at zero itself. */
+int cache_attend_noalloc(rkv_cache* c, int32_t layer, const void* q_bf16, const int32_t* q_pos,
+                         int32_t n_q, void* out_bf16, hipStream_t stream);
+
 /* One call of the per-chunk sequence (§2 "The step budget", Appendix G: each
  * call writes its new chunk, then attends over the whole cache):
  * cache_write_rope_fp8(k, v, pos, n) followed by cache_attend(q, q_pos,
