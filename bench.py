@@ -9,16 +9,18 @@ prepares the queries in the write's launch.  Every 42nd step is preceded by the
 position reset: a delta rotation of every cached key by -42 * 757.  The
 cache starts full with its ring head at slot 3,100 (8,888 tokens written).
 
-Prints one JSON line.  `value` is microseconds per step (= per attention call
-with its cache work, resets amortized).  The steps run first with eager
-launches (`components.eager_us_per_step`); when --steps is a whole number of
-42-step reset periods (the default 168), the same steps are then captured as
-one HIP graph per period (the device-side write position makes every call
-capturable) and replayed, and `value` is the replayed time (`launch` says
-which).  Per-operation times come from separate HIP-event-timed loops on the
-launch stream; `roofline` is the attention call (the dominant cost) against
-the dense FP8 matrix peak.  `cpu_baseline` times the NumPy float64 oracle on
-a bounded sample.
+Prints one JSON line.  `value` is microseconds per step (one write of 757
+tokens plus one attention call of 757 queries; the position reset, once per
+42 steps, is timed on its own and reported as `components.rotate_1layer_us`
+and its 42-step share `components.reset_share_us_per_step`).  The steps run
+first with eager launches (`components.eager_us_per_step`); the same number
+of steps is then captured as one HIP graph (the device-side write position
+makes every call capturable), replayed once untimed and once timed, and
+`value` is the replayed time (`launch` says which; --no-graph reports the
+eager one).  Per-operation times come from separate HIP-event-timed loops
+on the launch stream; `roofline` is the attention call (the dominant cost)
+against the dense FP8 matrix peak.  `cpu_baseline` times the NumPy float64
+oracle on the same work, median of 5.
 """
 from __future__ import annotations
 
@@ -47,7 +49,7 @@ PEAK_HBM_GBPS = 8000.0
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=168)
+    ap.add_argument("--steps", type=int, default=84)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--precision", choices=["precise", "fast"], default="precise")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -117,9 +119,14 @@ def timed(fn, reps, stream):
     return a.elapsed_time(b) / reps
 
 
-def cpu_baseline():
-    """The oracle on a bounded sample: one 757-token write (12 heads), attention of
-    the 757 queries on 2 of the 12 heads (scaled by 6), one-layer rotation / 42."""
+def cpu_baseline(runs=5):
+    """The oracle on the host cores, on the work of one step: one 757-token
+    write (12 heads), the attention of the 757 queries over the full
+    5,788-slot cache on all 12 heads, and one full-cache rotation (the reset,
+    once per 42 steps, reported apart).  Median of `runs` runs after one
+    warm-up, on the cache the bench's own writes produce."""
+    import statistics
+    import numpy
     from threadpoolctl import threadpool_info
     from oracle import attend as oatt, ring as oring
     from workloads import ATTEND, Stream, positions
@@ -133,41 +140,45 @@ def cpu_baseline():
         p0 += n
     q, k, v = s.chunk()
     pos = positions(8888, CHUNK)
-    t0 = time.perf_counter()
-    oring.write(st, k.f64, v.f64, pos)
-    t_write = time.perf_counter() - t0
-    sub = oring.RingState(N, 2, D, head=st.head, n_valid=st.n_valid, slot_pos=st.slot_pos,
-                          codes_k=st.codes_k[:2], codes_v=st.codes_v[:2],
-                          scale_k=st.scale_k[:2], scale_v=st.scale_v[:2])
-    t0 = time.perf_counter()
-    oatt.attend_exact(sub, q.f64[:, :2], pos)
-    t_attend = (time.perf_counter() - t0) * H / 2
-    t0 = time.perf_counter()
-    oring.rotate(st, -RESET_EVERY * CHUNK)
-    t_rot = time.perf_counter() - t0
+    parts = {"write": [], "attend": [], "rotate": []}
+    for r in range(runs + 1):
+        w = st.copy()
+        t0 = time.perf_counter()
+        oring.write(w, k.f64, v.f64, pos)
+        t1 = time.perf_counter()
+        oatt.attend_exact(w, q.f64, pos)
+        t2 = time.perf_counter()
+        oring.rotate(w, -RESET_EVERY * CHUNK)
+        t3 = time.perf_counter()
+        if r:  # the first run warms up
+            parts["write"].append(t1 - t0)
+            parts["attend"].append(t2 - t1)
+            parts["rotate"].append(t3 - t2)
+    med = {k2: statistics.median(v2) for k2, v2 in parts.items()}
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    per_step = t_write + t_attend + t_rot / RESET_EVERY
     return {
-        "value": per_step * 1e6,
+        "value": (med["write"] + med["attend"]) * 1e6,
         "unit": "us per step",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": ("NumPy float64 oracle on the host: one 757-token write (12 heads), "
-                   "attend_exact of the 757 queries on 2 of 12 heads scaled x6, one full "
-                   "5,788-slot rotation amortized over 42 steps"),
-        "parts_s": {"write": t_write, "attend_12h_est": t_attend, "rotate": t_rot},
+        "sample": ("NumPy float64 oracle on the host, the work of one step: one 757-token write (12 heads) "
+                   "and attend_exact of 757 queries over the full 5,788-slot cache, all 12 heads; "
+                   f"median of {runs} runs after a warm-up (the full-cache rotation, once per 42 steps, "
+                   "in parts_s)"),
+        "parts_s": {k2: round(v2, 5) for k2, v2 in med.items()},
         "host_cpus": os.cpu_count(),
+        "numpy": numpy.__version__,
     }
 
 
 def measured_peaks(stream):
     """The two ceilings measured on this device with the library's probes
-    (include/rkv_probe.h), reported beside the published peaks: dense FP8
+    (librkv_probe.so), reported beside the published peaks: dense FP8
     matrix throughput of the attention's instruction, and the HBM bandwidth
     of an in-place streaming read-modify-write (the rotation's pattern) over
     1 GiB, far beyond the 256 MB last-level cache (best of three timings)."""
     import torch
-    import fp8_ring_kv_amd as rkv
+    from fp8_ring_kv_amd import probe as rkv
     s = stream.cuda_stream
     wg, iters = 2048, 2000
     sink = torch.empty(wg, dtype=torch.float32, device="cuda:0")
@@ -184,10 +195,11 @@ def measured_peaks(stream):
                       "rkv_probe_stream (in-place read-modify-write of 1 GiB, 2 GiB moved)"}
 
 
-def capture_period(cache, pool, pos_pool, out):
-    """The 42 steps of a reset period (the rotation first) captured as ONE HIP
-    graph: the same kernels as the eager steps, one graph launch per period.
-    The device-side write position is what makes the calls capturable."""
+def capture_steps(cache, pool, pos_pool, out, first, steps):
+    """`steps` consecutive steps (from step index `first`) captured as ONE HIP
+    graph: the same calls as the eager steps, one graph launch for all of
+    them.  The device-side write position is what makes the calls
+    capturable; each replay advances the ring as the eager calls would."""
     import torch
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()
@@ -195,9 +207,8 @@ def capture_period(cache, pool, pos_pool, out):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
-            for j in range(RESET_EVERY):
-                if j == 0:
-                    cache.rotate(0, -RESET_EVERY * CHUNK)
+            for i in range(first, first + steps):
+                j = i % RESET_EVERY
                 q, k, v = pool[j]
                 cache.write_attend(0, k, v, pos_pool[j], q, pos_pool[j], out)
     stream.wait_stream(side)
@@ -224,10 +235,12 @@ def main():
     # starting state: 8,888 tokens written in 757-token chunks -> ring head at slot 3,100
     s = Stream(ATTEND)
     p0 = 0
+    fill = []
     while p0 < 8888:
         n = min(CHUNK, 8888 - p0)
         _, k, v = s.chunk(n)
-        cache.write(0, to_dev(k), to_dev(v), torch.from_numpy(positions(p0, n)).to(dev))
+        fill.append((to_dev(k), to_dev(v), torch.from_numpy(positions(p0, n)).to(dev)))
+        cache.write(0, *fill[-1])
         p0 += n
     torch.cuda.synchronize()
     assert int(cache.state(0)[0]) == 3100 and int(cache.state(0)[1]) == N
@@ -243,15 +256,13 @@ def main():
     # positions move back by 42 * 757, so new chunks reuse the same ones)
     pos_pool = [pos_base + (8888 + CHUNK * j) for j in range(RESET_EVERY)]
 
-    def step_fast(i):
+    def step(i):
         j = i % RESET_EVERY
-        if j == 0 and i > 0:
-            cache.rotate(0, -RESET_EVERY * CHUNK)
         q, k, v = pool[j]
         cache.write_attend(0, k, v, pos_pool[j], q, pos_pool[j], out)
 
     for i in range(args.warmup):
-        step_fast(i)
+        step(i)
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
@@ -259,7 +270,7 @@ def main():
     t_host0 = time.perf_counter()
     a.record(stream)
     for i in range(args.steps):
-        step_fast(args.warmup + i)
+        step(args.warmup + i)
     b.record(stream)
     b.synchronize()
     torch.cuda.synchronize()
@@ -267,26 +278,21 @@ def main():
     eager_ms = a.elapsed_time(b) / args.steps
     assert torch.isfinite(out.float()).all()
     ms_per_step, launch = eager_ms, "eager (one HIP launch per kernel)"
-    idx = args.warmup + args.steps
-    if not args.no_graph and args.steps % RESET_EVERY == 0:
-        # The same steps as captured reset periods: continue eagerly to a period
-        # boundary (untimed), capture one period, replay it once (untimed
-        # warm-up), then time exactly args.steps steps of replays.
-        while idx % RESET_EVERY:
-            step_fast(idx)
-            idx += 1
-        g = capture_period(cache, pool, pos_pool, out)
+    if not args.no_graph:
+        # The same number of steps captured as one graph, replayed once
+        # untimed (warm-up) and then once timed: exactly args.steps steps.
+        first = args.warmup + args.steps
+        g = capture_steps(cache, pool, pos_pool, out, first, args.steps)
         g.replay()
         torch.cuda.synchronize()
         a.record(stream)
-        for _ in range(args.steps // RESET_EVERY):
-            g.replay()
+        g.replay()
         b.record(stream)
         b.synchronize()
         torch.cuda.synchronize()
         assert torch.isfinite(out.float()).all()
         ms_per_step = a.elapsed_time(b) / args.steps
-        launch = "hip_graph (one graph per 42-step reset period, replayed)"
+        launch = f"hip_graph ({args.steps} steps captured as one graph, replayed)"
         del g
 
     if args.copy_mib:
@@ -304,6 +310,14 @@ def main():
         r = args.reps
         q0, k0, v0 = pool[0]
         comp["attend_us"] = 1e3 * timed(lambda: cache.attend(0, q0, pos_pool[0], out), r, stream)
+        # the other precision on a cache holding the same tokens
+        other = rkv.RKV_FAST if prec == rkv.RKV_PRECISE else rkv.RKV_PRECISE
+        twin = rkv.RingCache(1, N, H, D, CHUNK, other, device=dev, attn_workgroups=args.workgroups)
+        for kvp in fill:
+            twin.write(0, *kvp)
+        key = "attend_fast_us" if other == rkv.RKV_FAST else "attend_precise_us"
+        comp[key] = 1e3 * timed(lambda: twin.attend(0, q0, pos_pool[0], out), r, stream)
+        del twin
         comp["write_us"] = 1e3 * timed(lambda: cache.write(0, k0, v0, pos_pool[0]), r, stream)
         comp["attend_TFLOPs"] = ATTN_FLOP / comp["attend_us"] / 1e6
         comp["write_GBps"] = WRITE_BYTES / comp["write_us"] / 1e3
@@ -315,6 +329,7 @@ def main():
             flip[0] = -flip[0]
         comp["rotate_1layer_us"] = 1e3 * timed(rot, max(20, r // 4), stream)
         comp["rotate_1layer_GBps"] = ROTATE_BYTES / comp["rotate_1layer_us"] / 1e3
+        comp["reset_share_us_per_step"] = comp["rotate_1layer_us"] / RESET_EVERY
         # 60 stacked layer caches (1.1 GB): rotation of every layer in one launch,
         # and writes cycling over the layers -- both far beyond the 256 MB cache
         big = rkv.RingCache(60, N, H, D, CHUNK, prec, device=dev)
@@ -419,7 +434,7 @@ def main():
     res = {
         "metric": "µs per attention call (757q×5788 FP8 KV) + cache-write GB/s; % of roofline",
         "value": round(ms_per_step * 1e3, 3),
-        "unit": "us per call (write 757 tokens + attend 757 queries; resets amortized)",
+        "unit": "us per step (write 757 tokens + attend 757 queries)",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

@@ -24,7 +24,7 @@ __all__ = [
     "ring_cache_bytes", "ring_cache_create", "ring_cache_destroy", "ring_cache_reset",
     "ring_cache_layout", "cache_write_rope_fp8", "cache_delta_rotate", "cache_attend", "cache_attend_noalloc",
     "cache_write_attend", "ring_cache_set_qk_norm", "ring_cache_calibrate_static",
-    "rkv_last_error", "rkv_probe_fp8_mfma", "rkv_probe_stream", "RingCache",
+    "rkv_last_error", "RingCache",
 ]
 
 RKV_OK, RKV_EINVAL, RKV_EHIP = 0, -1, -2
@@ -111,10 +111,6 @@ def lib() -> ctypes.CDLL:
     L.ring_cache_calibrate_static.argtypes = [VP, I32, ctypes.c_float, VP]
     L.ring_cache_calibrate_static.restype = ctypes.c_int
     L.ring_cache_set_qk_norm.restype = ctypes.c_int
-    L.rkv_probe_fp8_mfma.argtypes = [I32, I32, VP, VP]
-    L.rkv_probe_fp8_mfma.restype = ctypes.c_int
-    L.rkv_probe_stream.argtypes = [VP, SZ, VP]
-    L.rkv_probe_stream.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -203,20 +199,6 @@ def ring_cache_calibrate_static(handle: int, layer: int, margin: float, stream: 
     rc = lib().ring_cache_calibrate_static(ctypes.c_void_p(handle), layer, margin, ctypes.c_void_p(stream))
     if rc != RKV_OK:
         raise RkvError(rc, "ring_cache_calibrate_static")
-
-
-# ---- measurement aids (include/rkv_probe.h) ----------------------------------
-
-def rkv_probe_fp8_mfma(workgroups: int, iters: int, sink: int, stream: int) -> None:
-    rc = lib().rkv_probe_fp8_mfma(workgroups, iters, ctypes.c_void_p(sink), ctypes.c_void_p(stream))
-    if rc != RKV_OK:
-        raise RkvError(rc, "rkv_probe_fp8_mfma")
-
-
-def rkv_probe_stream(buf: int, nbytes: int, stream: int) -> None:
-    rc = lib().rkv_probe_stream(ctypes.c_void_p(buf), nbytes, ctypes.c_void_p(stream))
-    if rc != RKV_OK:
-        raise RkvError(rc, "rkv_probe_stream")
 
 
 # ---- torch-facing wrapper ---------------------------------------------------

@@ -16,7 +16,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "librkv.so")
 OBJ = os.path.join(ROOT, "_build")
-SOURCES = ["rkv_api.cpp", "k_cache.hip", "k_attend.hip", "k_probe.hip"]
+SOURCES = ["rkv_api.cpp", "k_cache.hip", "k_attend.hip"]
+# the benchmark's measurement aids: a library of their own, outside the cache ABI
+PROBE_OUT = os.path.join(PKG, "librkv_probe.so")
+PROBE_SOURCES = ["probe/k_probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",
@@ -45,27 +48,35 @@ def hipcc() -> str:
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    obj = os.path.join(OBJ, os.path.splitext(os.path.basename(src))[0] + ".o")
+    extra = ["-I", os.path.join(CSRC, "probe")] if src.startswith("probe/") else []
+    cmd = [hipcc(), *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link librkv.so; returns its path."""
-    os.makedirs(OBJ, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link librkv.so and librkv_probe.so; returns the
+    path of librkv.so."""
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[: len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], PROBE_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {PROBE_OUT}")
     return OUT
 
 

@@ -1,6 +1,13 @@
 // Measurement kernels for the two ceilings of the cache kernels on gfx950:
-// dense FP8 matrix throughput and the HBM bandwidth of an in-place stream.
-#include "rkv_launch.h"
+// dense FP8 matrix throughput and the HBM bandwidth of an in-place stream,
+// with their C ABI (rkv_probe.h).  Built into librkv_probe.so, a library of
+// its own beside the cache library: these are measurement aids of the
+// benchmark, not steps of the cache method.
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "rkv_probe.h"
 
 namespace rkv {
 
@@ -50,12 +57,12 @@ __global__ __launch_bounds__(256) void probe_stream_kernel(u4v* p, long long n16
   }
 }
 
-hipError_t launch_probe_mfma(int workgroups, int iters, float* sink, hipStream_t s) {
+static hipError_t launch_probe_mfma(int workgroups, int iters, float* sink, hipStream_t s) {
   hipLaunchKernelGGL(probe_mfma_kernel, dim3(workgroups), dim3(256), 0, s, iters, sink);
   return hipGetLastError();
 }
 
-hipError_t launch_probe_stream(void* buf, size_t bytes, hipStream_t s) {
+static hipError_t launch_probe_stream(void* buf, size_t bytes, hipStream_t s) {
   const long long n16 = (long long)(bytes / 16);
   // one 16 KiB block per workgroup up to 65,536 workgroups (1 GiB); larger
   // buffers loop.  Many short workgroups measured faster than a persistent
@@ -67,3 +74,37 @@ hipError_t launch_probe_stream(void* buf, size_t bytes, hipStream_t s) {
 }
 
 }  // namespace rkv
+
+namespace {
+thread_local std::string g_probe_err;
+int probe_fail(int code, const std::string& msg) {
+  g_probe_err = msg;
+  return code;
+}
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+}  // namespace
+
+extern "C" {
+
+const char* rkv_probe_last_error(void) { return g_probe_err.c_str(); }
+
+int rkv_probe_fp8_mfma(int32_t workgroups, int32_t iters, float* sink, hipStream_t stream) {
+  if (!sink) return probe_fail(RKV_PROBE_EINVAL, "sink is null");
+  if (!aligned(sink, 4)) return probe_fail(RKV_PROBE_EINVAL, "sink must be 4-byte aligned");
+  if (workgroups < 1 || workgroups > 65536) return probe_fail(RKV_PROBE_EINVAL, "workgroups outside [1, 65536]");
+  if (iters < 1 || iters > (1 << 20)) return probe_fail(RKV_PROBE_EINVAL, "iters outside [1, 2^20]");
+  hipError_t e = rkv::launch_probe_mfma(workgroups, iters, sink, stream);
+  if (e != hipSuccess) return probe_fail(RKV_PROBE_EHIP, std::string("mfma probe launch: ") + hipGetErrorString(e));
+  return 0;
+}
+
+int rkv_probe_stream(void* buf, size_t bytes, hipStream_t stream) {
+  if (!buf) return probe_fail(RKV_PROBE_EINVAL, "buf is null");
+  if (!aligned(buf, 16)) return probe_fail(RKV_PROBE_EINVAL, "buf must be 16-byte aligned");
+  if (bytes == 0 || bytes % 16 != 0) return probe_fail(RKV_PROBE_EINVAL, "bytes must be a positive multiple of 16");
+  hipError_t e = rkv::launch_probe_stream(buf, bytes, stream);
+  if (e != hipSuccess) return probe_fail(RKV_PROBE_EHIP, std::string("stream probe launch: ") + hipGetErrorString(e));
+  return 0;
+}
+
+}  // extern "C"

@@ -1,5 +1,6 @@
 /*
- * rkv_probe.h -- measurement aids of the librkv library for MI355X (gfx950).
+ * rkv_probe.h -- measurement aids for MI355X (gfx950), in librkv_probe.so,
+ * a library of their own beside the cache library librkv.so.
  *
  * These are not steps of the cache method: they measure the two ceilings
  * that bound its kernels on the running device, so that a benchmark can
@@ -12,10 +13,10 @@
  *                          read-modify-write, the access pattern of the
  *                          delta rotation (nontemporal 16-byte accesses).
  *
- * Conventions are those of rkv.h: the caller owns every buffer, calls only
- * enqueue work on the given stream, host-visible misuse returns RKV_EINVAL
- * (with a message in rkv_last_error()) and enqueues nothing, a failed
- * launch returns RKV_EHIP.  Time the calls with events on the same stream.
+ * The caller owns every buffer, calls only enqueue work on the given
+ * stream, host-visible misuse returns RKV_PROBE_EINVAL (with a message in
+ * rkv_probe_last_error()) and enqueues nothing, a failed launch returns
+ * RKV_PROBE_EHIP.  Time the calls with events on the same stream.
  */
 #ifndef RKV_PROBE_H
 #define RKV_PROBE_H
@@ -28,6 +29,11 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+enum { RKV_PROBE_EINVAL = -1, RKV_PROBE_EHIP = -2 };
+
+/* Message for the last error of a probe call on the calling thread. */
+const char* rkv_probe_last_error(void);
 
 /* Runs `workgroups` workgroups of 4 waves; every wave issues `iters` rounds
  * of 4 independent v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 operands, neutral

@@ -2,7 +2,6 @@
 // launches.  No device allocation, no stream synchronization, no host read
 // of device state (see include/rkv.h).
 #include "rkv.h"
-#include "rkv_probe.h"
 
 #include <cmath>
 #include <cstring>
@@ -403,27 +402,6 @@ int ring_cache_calibrate_static(rkv_cache* c, int32_t layer, float margin, hipSt
   hipError_t e = rkv::launch_calibrate(c->g, lo, hi, margin, stream);
   if (e != hipSuccess) return hip_fail(e, "calibrate kernel launch");
   g_err.clear();
-  return RKV_OK;
-}
-
-// ---- measurement aids (include/rkv_probe.h) ----
-
-int rkv_probe_fp8_mfma(int32_t workgroups, int32_t iters, float* sink, hipStream_t stream) {
-  if (!sink) return fail(RKV_EINVAL, "sink is null");
-  if (!aligned(sink, 4)) return fail(RKV_EINVAL, "sink must be 4-byte aligned");
-  if (workgroups < 1 || workgroups > 65536) return fail(RKV_EINVAL, "workgroups outside [1, 65536]");
-  if (iters < 1 || iters > (1 << 20)) return fail(RKV_EINVAL, "iters outside [1, 2^20]");
-  hipError_t e = rkv::launch_probe_mfma(workgroups, iters, sink, stream);
-  if (e != hipSuccess) return hip_fail(e, "mfma probe launch");
-  return RKV_OK;
-}
-
-int rkv_probe_stream(void* buf, size_t bytes, hipStream_t stream) {
-  if (!buf) return fail(RKV_EINVAL, "buf is null");
-  if (!aligned(buf, 16)) return fail(RKV_EINVAL, "buf must be 16-byte aligned");
-  if (bytes == 0 || bytes % 16 != 0) return fail(RKV_EINVAL, "bytes must be a positive multiple of 16");
-  hipError_t e = rkv::launch_probe_stream(buf, bytes, stream);
-  if (e != hipSuccess) return hip_fail(e, "stream probe launch");
   return RKV_OK;
 }
 

@@ -28,9 +28,6 @@ struct AttnWs {
 };
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
-// Measurement kernels (include/rkv_probe.h).
-hipError_t launch_probe_mfma(int workgroups, int iters, float* sink, hipStream_t s);
-hipError_t launch_probe_stream(void* buf, size_t bytes, hipStream_t s);
 hipError_t launch_init_consts(const Geom& g, const double* turns, int n, hipStream_t s);
 hipError_t launch_reset(const Geom& g, int layer_lo, int layer_hi, hipStream_t s);
 // Static per-head scales from the valid cache of each layer in [layer_lo, layer_hi).

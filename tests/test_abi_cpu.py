@@ -34,10 +34,24 @@ def test_every_declared_symbol_is_exported():
     assert set(names) >= {"ring_cache_bytes", "ring_cache_create", "ring_cache_destroy",
                           "ring_cache_reset", "ring_cache_layout", "cache_write_rope_fp8",
                           "cache_delta_rotate", "cache_attend", "cache_write_attend", "rkv_last_error",
-                          "rkv_probe_fp8_mfma", "rkv_probe_stream"}
+                          "cache_attend_noalloc", "ring_cache_calibrate_static", "ring_cache_set_qk_norm"}
     L = rkv.lib()
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_measurement_probes_live_outside_the_cache_library():
+    """The benchmark's probes are a library of their own (librkv_probe.so,
+    declared in csrc/probe/rkv_probe.h): exported there, not by librkv.so."""
+    from fp8_ring_kv_amd import probe
+    path = os.path.join(ROOT, "fp8_ring_kv_amd", "csrc", "probe", "rkv_probe.h")
+    text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+    names = set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(rkv_probe_[a-z0-9_]*)\s*\(", text, flags=re.M))
+    assert names == {"rkv_probe_fp8_mfma", "rkv_probe_stream", "rkv_probe_last_error"}
+    P = probe.lib()
+    for n in names:
+        assert hasattr(P, n), n
+        assert not hasattr(rkv.lib(), n), n
 
 
 def test_single_hip_runtime_in_process():
@@ -110,16 +124,17 @@ def test_calls_on_null_cache_are_einval():
 def test_probes_reject_misuse_without_launching():
     """The measurement aids validate their arguments on the host: nothing
     below reaches a kernel launch (no GPU here)."""
-    L = rkv.lib()
+    from fp8_ring_kv_amd import probe
+    L = probe.lib()
     fake = ctypes.c_void_p(0x100000)  # never dereferenced: every call fails validation first
-    assert L.rkv_probe_fp8_mfma(1, 1, None, None) == rkv.RKV_EINVAL
-    assert L.rkv_probe_fp8_mfma(0, 1, fake, None) == rkv.RKV_EINVAL
-    assert L.rkv_probe_fp8_mfma(65537, 1, fake, None) == rkv.RKV_EINVAL
-    assert L.rkv_probe_fp8_mfma(1, 0, fake, None) == rkv.RKV_EINVAL
-    assert L.rkv_probe_fp8_mfma(1, (1 << 20) + 1, fake, None) == rkv.RKV_EINVAL
-    assert L.rkv_probe_fp8_mfma(1, 1, ctypes.c_void_p(0x100002), None) == rkv.RKV_EINVAL
-    assert L.rkv_probe_stream(None, 16, None) == rkv.RKV_EINVAL
-    assert L.rkv_probe_stream(ctypes.c_void_p(0x100008), 16, None) == rkv.RKV_EINVAL
-    assert L.rkv_probe_stream(fake, 0, None) == rkv.RKV_EINVAL
-    assert L.rkv_probe_stream(fake, 24, None) == rkv.RKV_EINVAL
-    assert "multiple of 16" in rkv.rkv_last_error()
+    assert L.rkv_probe_fp8_mfma(1, 1, None, None) == -1
+    assert L.rkv_probe_fp8_mfma(0, 1, fake, None) == -1
+    assert L.rkv_probe_fp8_mfma(65537, 1, fake, None) == -1
+    assert L.rkv_probe_fp8_mfma(1, 0, fake, None) == -1
+    assert L.rkv_probe_fp8_mfma(1, (1 << 20) + 1, fake, None) == -1
+    assert L.rkv_probe_fp8_mfma(1, 1, ctypes.c_void_p(0x100002), None) == -1
+    assert L.rkv_probe_stream(None, 16, None) == -1
+    assert L.rkv_probe_stream(ctypes.c_void_p(0x100008), 16, None) == -1
+    assert L.rkv_probe_stream(fake, 0, None) == -1
+    assert L.rkv_probe_stream(fake, 24, None) == -1
+    assert "multiple of 16" in probe.rkv_probe_last_error()

@@ -1,11 +1,11 @@
-"""GPU checks of the measurement aids (include/rkv_probe.h): each computes
+"""GPU checks of the measurement aids (librkv_probe.so, csrc/probe/rkv_probe.h): each computes
 what its header states, so the peaks the benchmark reports beside the
 published ones come from the stated work."""
 import numpy as np
 import pytest
 import torch
 
-import fp8_ring_kv_amd as rkv
+from fp8_ring_kv_amd import probe as rkv
 from tests.gpu_common import DEV, require_gpu
 
 pytestmark = pytest.mark.gpu
