@@ -426,6 +426,10 @@ def main():
         # (amax x 1.5), then the same write and rotation with fixed scales
         cache.calibrate_static(0, 1.5)
         comp["write_static_us"] = 1e3 * timed(lambda: cache.write(0, k0, v0, pos_pool[0]), r, stream)
+        # attention with the static scales (s_k folded into the queries, s_v
+        # after the product, no per-slot scale reads)
+        comp["attend_static_us"] = 1e3 * timed(lambda: cache.attend(0, q0, pos_pool[0], out), r, stream)
+        comp["attend_static_TFLOPs"] = ATTN_FLOP / comp["attend_static_us"] / 1e6
         comp["rotate_static_1layer_us"] = 1e3 * timed(rot, max(20, r // 4), stream)
         cache.reset(0)
         torch.cuda.synchronize()
@@ -464,6 +468,12 @@ def main():
                            "per_launch_us": round(comp["attend_us"], 3)}
         if peaks:
             res["roofline"]["frac_of_measured_peak"] = round(achieved / peaks["fp8_mfma_TFLOPs"], 4)
+    if "attend_static_us" in comp:
+        a2 = comp["attend_static_TFLOPs"]
+        res["roofline_static"] = {"workload": "attend_757x5788_h12, static per-head scales (calibrated x1.5)",
+                                  "bound": "mfma", "achieved": round(a2, 2), "peak": PEAK_FP8_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(a2 / PEAK_FP8_TFLOPS, 4),
+                                  "per_launch_flop": ATTN_FLOP, "per_launch_us": round(comp["attend_static_us"], 3)}
     if "rotate_60layer_GBps" in comp:
         res["roofline_hbm"] = {
             "write": {"achieved": round(comp["write_GBps"], 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",

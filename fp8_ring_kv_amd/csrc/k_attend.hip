@@ -50,6 +50,7 @@
 // e4m3 subnormal range, where the second term still carries them.)
 #include <cmath>
 #include <mutex>
+#include <type_traits>
 
 #include "rkv_launch.h"
 #include "write_body.h"
@@ -128,6 +129,7 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;  // LDS byte, addresse
 constexpr double kLog2e = 1.4426950408889634;  // log2(e)
 constexpr float kLazy = 6.f;             // log2 headroom of the running maximum
 constexpr float kHeadroom = 64.f;        // 2^kLazy: c_h = 448 / (kHeadroom vmax_h)
+constexpr float kLog2Seven = 2.8073549f; // log2(448 / kHeadroom): static scales feed P' = 7 P
 constexpr int kQG = 128;      // queries per unit: 4 waves x 32
 
 // Terms of the two precisions (TERMS = 2: precise, 1: fast).  Precise mode
@@ -256,8 +258,9 @@ __device__ inline void copy16(const void* gp, lds_u8* lp) {
 }
 
 // Copy tile T of the head into an LDS buffer (this wave's share: the same
-// number of copy instructions in every wave, TileLds::COPIES).
-template <int D>
+// number of copy instructions in every wave).  With static scales (ST) the
+// per-slot scales are not needed and not copied.
+template <int D, bool ST = false>
 __device__ inline void copy_tile(lds_u8* lbuf, const TileSrc& src, int T, const CopyOffsets<D>& co,
                                  int wave, int lane) {
   constexpr int KC = TileLds<D>::KC;
@@ -271,8 +274,10 @@ __device__ inline void copy_tile(lds_u8* lbuf, const TileSrc& src, int T, const 
   }
   // scales: waves 0, 1 copy s_k[32 w, +32), waves 2, 3 s_v[32 (w - 2), +32),
   // 4 per lane on lanes 0..7
-  const float* sb = (wave < 2 ? src.skb : src.svb) + T * kTile + 32 * (wave & 1);
-  if (lane < 8) copy16(sb + 4 * lane, lbuf + TileLds<D>::S_OFF + 128 * wave);
+  if constexpr (!ST) {
+    const float* sb = (wave < 2 ? src.skb : src.svb) + T * kTile + 32 * (wave & 1);
+    if (lane < 8) copy16(sb + 4 * lane, lbuf + TileLds<D>::S_OFF + 128 * wave);
+  }
 }
 
 // Wait until at most N of this wave's vector memory operations are in flight
@@ -380,7 +385,11 @@ struct WaveState {
 // running sum l accumulates P' (so the output is O / l).  The key and value
 // scales of the 16 slots of a lane's half arrive as 16-byte LDS reads that
 // every lane of the half shares, one value per accumulator register.
-template <int D, int TERMS>
+// ST (the pages' static per-head scales, every valid slot of the head
+// carrying them): s_k is already in the queries, so y - mc = S - mc, and
+// l2c = log2 7, so P' = 7 P is fed as x directly (7 = 448 / 64, the
+// headroom); s_v is applied once to the output.  No per-slot scale is read.
+template <int D, int TERMS, bool ST>
 __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>& st,
                                   unsigned long long mask, float l2c, int lane, const lds_u8* sp) {
   // x = P' s_v is formed once and reused; contracting x - e4m3(x) into
@@ -393,18 +402,26 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
   // before the first tile there is no max: scores relative to 0, and the
   // first tile always raises the max
   const float mcu = st.m == -INFINITY ? 0.f : st.m - l2c;
-  v4f sk[8];  // all eight reads issued before the first use
-#pragma unroll
-  for (int w = 0; w < 8; ++w) sk[w] = *reinterpret_cast<lds_v4f*>(sp + 128 * (w >> 2) + 16 * (w & 3));
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    const int sub = w >> 2, r0 = 4 * (w & 3);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[sub][r0 + e] = __builtin_fmaf(acc[sub][r0 + e], sk[w][e], -mcu);
-  }
   v4f sv[8];  // value scales, read while the max is found
+  if constexpr (ST) {
 #pragma unroll
-  for (int w = 0; w < 8; ++w) sv[w] = *reinterpret_cast<lds_v4f*>(sp + 256 + 128 * (w >> 2) + 16 * (w & 3));
+    for (int r = 0; r < 16; ++r) {
+      acc[0][r] -= mcu;
+      acc[1][r] -= mcu;
+    }
+  } else {
+    v4f sk[8];  // all eight reads issued before the first use
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sk[w] = *reinterpret_cast<lds_v4f*>(sp + 128 * (w >> 2) + 16 * (w & 3));
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int sub = w >> 2, r0 = 4 * (w & 3);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[sub][r0 + e] = __builtin_fmaf(acc[sub][r0 + e], sk[w][e], -mcu);
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sv[w] = *reinterpret_cast<lds_v4f*>(sp + 256 + 128 * (w >> 2) + 16 * (w & 3));
+  }
   if (mask != ~0ull) {  // partially valid tile (ring edge, partial fill, padding)
     const uint32_t m0 = (uint32_t)(mask >> (16 * gq)) & 0xFFFFu;  // slots 16 gq + r
     const uint32_t m1 = (uint32_t)(mask >> (32 + 16 * gq)) & 0xFFFFu;
@@ -443,7 +460,8 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
     for (int e = 0; e < 4; ++e) {
       const float p = __builtin_amdgcn_exp2f(acc[sub][r0 + e]);
       st.l += p;
-      x[e] = p * sv[w][e];
+      if constexpr (ST) x[e] = p;
+      else x[e] = p * sv[w][e];
     }
     // (the low-half conversion keeps the high half of its third operand,
     // which the high-half conversion overwrites: any value will do)
@@ -493,6 +511,7 @@ struct QPrepArgs {
   float qscale;  // softmax scale in log2 units, log2(e) / sqrt(D), rounded once to float
   const uint16_t* wq;  // query RMS-norm weights (bf16 [D]) of the fused pre-attention norm, null when off
   float eps;           // its epsilon
+  int layer;           // the cache layer (its static scales, when calibrated)
 };
 
 // Body of one 256-thread workgroup number `block` of the preparation.
@@ -540,6 +559,13 @@ __device__ inline void q_prep_body(const QPrepArgs& A, int block) {
       for (int e = 0; e < 8; ++e) xs[8 * c + e] = xs[8 * c + e] * rn * wv[e];
     }
   }
+  // With the pages' static scales the head's key scale is folded into the
+  // query, so the products with the key codes come out in log2 units.
+  float qsc = A.qscale;
+  {
+    const LayerPtrs L = layer_ptrs(A.g, A.layer);
+    if (static_head(L, H, h)) qsc = A.qscale * L.stat[h];
+  }
   float y[EPT];
   float am = 0.f;
 #pragma unroll
@@ -549,8 +575,8 @@ __device__ inline void q_prep_body(const QPrepArgs& A, int block) {
       float cs, sn;
       rope_cs(p, turns[4 * c + m], cs, sn);
       const float x0 = xs[8 * c + 2 * m], x1 = xs[8 * c + 2 * m + 1];
-      y[8 * c + 2 * m] = (x0 * cs - x1 * sn) * A.qscale;
-      y[8 * c + 2 * m + 1] = (x0 * sn + x1 * cs) * A.qscale;
+      y[8 * c + 2 * m] = (x0 * cs - x1 * sn) * qsc;
+      y[8 * c + 2 * m + 1] = (x0 * sn + x1 * cs) * qsc;
       am = fmaxf(am, fmaxf(fabsf(y[8 * c + 2 * m]), fabsf(y[8 * c + 2 * m + 1])));
     }
   }
@@ -879,7 +905,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
     for (int k2 = 0; k2 < kSub; ++k2) vm = max(vm, L.vmax[h * kSub + k2]);
     const float vmaxh = __uint_as_float(vm);
     const float ch = vmaxh > 0.f ? kE4M3Max / (kHeadroom * vmaxh) : 1.f;
-    const float l2c = __log2f(ch);
+    // the pages' static per-head scales (every valid slot of the head
+    // carries them): P' = 7 P with no per-slot factor, s_v on the output
+    const bool sh = static_head(L, H, h);
+    const float svh = sh ? L.stat[H + h] : 1.f;
+    const float l2c = sh ? kLog2Seven : __log2f(ch);
     TileSrc src;
     src.kbase = L.codes_k + (size_t)h * NP * D;
     src.vbase = L.codes_v + (size_t)h * NT * D * kTile;
@@ -891,7 +921,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
     //         the first pair of tiles ----
     const int qi = kQG * qg + 32 * wave + li;
     if (u != u_pre) load_q(u);
-    for (int tj = 0; tj < 2 && tj < nk; ++tj) copy_tile<D>(buf(tj), src, tile_of(t_lo + tj), coff, wave, lane);
 
     // ---- 2. the segment's tiles, in pairs.  Tile t sits in buffer t % 4.
     //         One barrier per pair: after it, the pair's tiles have landed and
@@ -902,34 +931,41 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
     st.l = 0.f;
 #pragma unroll
     for (int b = 0; b < DB; ++b) st.O[b] = v16f{};
-    for (int j = 0; j < nk; ++j) {
-      if ((j & 1) == 0) {
-        // a new pair of tiles: tiles j, j + 1 have landed and every wave is
-        // done with the previous pair, whose buffers take the next pair
-        wait_copies_and_barrier<0>();
-        set_progress_priority(j, nk);
-        if (j + 2 < nk) copy_tile<D>(buf(j + 2), src, tile_of(t_lo + j + 2), coff, wave, lane);
-        if (j + 3 < nk) copy_tile<D>(buf(j + 3), src, tile_of(t_lo + j + 3), coff, wave, lane);
+    auto run_tiles = [&](auto static_tag) {
+      constexpr bool ST = decltype(static_tag)::value;
+      for (int tj = 0; tj < 2 && tj < nk; ++tj)
+        copy_tile<D, ST>(buf(tj), src, tile_of(t_lo + tj), coff, wave, lane);
+      for (int j = 0; j < nk; ++j) {
+        if ((j & 1) == 0) {
+          // a new pair of tiles: tiles j, j + 1 have landed and every wave is
+          // done with the previous pair, whose buffers take the next pair
+          wait_copies_and_barrier<0>();
+          set_progress_priority(j, nk);
+          if (j + 2 < nk) copy_tile<D, ST>(buf(j + 2), src, tile_of(t_lo + j + 2), coff, wave, lane);
+          if (j + 3 < nk) copy_tile<D, ST>(buf(j + 3), src, tile_of(t_lo + j + 3), coff, wave, lane);
+        }
+        const lds_u8* lb = buf(j);
+        KOp<D> kf;
+        VOp<D> vf;
+        v16f sacc[2];
+        read_k<D>(kf, lb, off);
+        qk<D, QT>(sacc, kf, qf, qs);
+        read_v<D>(vf, lb, off);
+        // Only the first and last tiles of the valid range and the ring's last
+        // tile (pad slots) can hold invalid slots: the others skip the mask.
+        const int T = tile_of(t_lo + j);
+        unsigned long long mask = ~0ull;
+        if (t_lo + j == 0 || t_lo + j == count - 1 || T == NT - 1) {
+          const int sl = T * kTile + lane;
+          int rel = sl - a;
+          if (rel < 0) rel += N;
+          mask = __ballot(sl < N && rel < nv);
+        }
+        softmax_pv<D, TERMS, ST>(sacc, vf, st, mask, l2c, lane, lb + off.sk4);
       }
-      const lds_u8* lb = buf(j);
-      KOp<D> kf;
-      VOp<D> vf;
-      v16f sacc[2];
-      read_k<D>(kf, lb, off);
-      qk<D, QT>(sacc, kf, qf, qs);
-      read_v<D>(vf, lb, off);
-      // Only the first and last tiles of the valid range and the ring's last
-      // tile (pad slots) can hold invalid slots: the others skip the mask.
-      const int T = tile_of(t_lo + j);
-      unsigned long long mask = ~0ull;
-      if (t_lo + j == 0 || t_lo + j == count - 1 || T == NT - 1) {
-        const int sl = T * kTile + lane;
-        int rel = sl - a;
-        if (rel < 0) rel += N;
-        mask = __ballot(sl < N && rel < nv);
-      }
-      softmax_pv<D, TERMS>(sacc, vf, st, mask, l2c, lane, lb + off.sk4);
-    }
+    };
+    if (sh) run_tiles(std::true_type{});
+    else run_tiles(std::false_type{});
 
     __builtin_amdgcn_s_setprio(0);
 
@@ -937,7 +973,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
     const float Lw = half_swap_add(st.l);
     uint16_t* orow = A.out + ((size_t)qi * H + h) * D;
     if (t_lo == 0 && t_hi == count) {
-      if (qi < A.n_q) store_rows<DB>(orow, st.O, Lw > 0.f ? 1.f / Lw : 0.f, gq);
+      if (qi < A.n_q) store_rows<DB>(orow, st.O, Lw > 0.f ? svh / Lw : 0.f, gq);
     } else {
       // Partial id gi + u is distinct for every (workgroup, unit) pair: ranges
       // are ordered, so a later workgroup never meets an earlier unit.  The
@@ -951,7 +987,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
       // after the counter says every segment has stored.
       const int seg = gi + u;
       const PartRsrc pr = PartRsrc::make<D>(A.ws, G + U);
-      store_partial<D>(pr, (seg * kWaves + wave) * (D / 16) * 64 + lane, st.O, Lw > 0.f ? ch / Lw : 0.f);
+      // (static scales: O / l is 7 P-weighted codes, and c_h s_v / l makes the
+      // merge's final 1 / (c_h l) give s_v O / l)
+      store_partial<D>(pr, (seg * kWaves + wave) * (D / 16) * 64 + lane, st.O, Lw > 0.f ? ch * svh / Lw : 0.f);
       store_ml(pr, (seg * kWaves + wave) * 64 + lane, st.m, Lw);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
@@ -1029,9 +1067,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
   }
 }
 
-static QPrepArgs make_prep_args(const Geom& g, const AttnWs& ws, const void* q, const int32_t* q_pos, int n_q,
-                                const uint16_t* wq, float eps) {
+static QPrepArgs make_prep_args(const Geom& g, const AttnWs& ws, int layer, const void* q, const int32_t* q_pos,
+                                int n_q, const uint16_t* wq, float eps) {
   QPrepArgs P;
+  P.layer = layer;
   P.wq = wq;
   P.eps = eps;
   P.g = g;
@@ -1093,7 +1132,7 @@ static hipError_t launch_attend_main(const Geom& g, const AttnWs& ws, int layer,
 hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void* q,
                          const int32_t* q_pos, int n_q, void* out, const uint16_t* wq, float eps,
                          hipStream_t s) {
-  const QPrepArgs P = make_prep_args(g, ws, q, q_pos, n_q, wq, eps);
+  const QPrepArgs P = make_prep_args(g, ws, layer, q, q_pos, n_q, wq, eps);
   const dim3 pgrid(prep_blocks(P));
   if (g.head_dim == 128) {
     if (ws.terms == 2) hipLaunchKernelGGL((q_prep_kernel<128, 2>), pgrid, dim3(256), 0, s, P);
@@ -1122,7 +1161,7 @@ hipError_t launch_write_attend(const Geom& g, const AttnWs& ws, int layer, const
     return launch_attend(g, ws, layer, q, q_pos, n_q, out, wq, eps, s);
   }
   WritePrepArgs W;
-  W.P = make_prep_args(g, ws, q, q_pos, n_q, wq, eps);
+  W.P = make_prep_args(g, ws, layer, q, q_pos, n_q, wq, eps);
   W.wk = wk;
   W.layer = layer;
   W.k = (const uint4*)k;

@@ -75,10 +75,11 @@ hipError_t launch_reset(const Geom& g, int layer_lo, int layer_hi, hipStream_t s
 // Static-scale calibration, the pages' own scale mode (Appendix G; §4.3 "FP8
 // at write"): per (layer, head), amax = the largest magnitude of the
 // dequantized keys (values) over the valid slots, s = fp32(margin amax / 448);
-// then the layer's flag is set and later writes quantize with these scales
-// and reset rotations requantize each head's keys with its key scale (a head
-// at amax 0 gets scale 0, which the write and the rotation read as "keep the
-// per-(token, head) rule").  One workgroup per (head, layer) scans the
+// then the head's valid cache is requantized with these scales, the layer's
+// flag is set, and later writes quantize with these scales and reset
+// rotations requantize each head's keys with its key scale (a head at amax
+// 0 gets scale 0, which the write, the rotation and the attention read as
+// "keep the per-(token, head) rule").  One workgroup per (head, layer) scans the
 // head's codes 16 bytes per thread.  The products code * scale are exact in
 // double precision and the scale is formed as margin * amax / 448 in double,
 // rounded once to float.
@@ -133,11 +134,86 @@ __global__ __launch_bounds__(256) void calibrate_kernel(Geom g, int layer_lo, fl
     }
     __syncthreads();
   }
+  const float sk = (float)((double)margin * red[0][0] / (double)kE4M3Max);
+  const float sv = (float)((double)margin * red[1][0] / (double)kE4M3Max);
   if (threadIdx.x == 0) {
-    L.stat[h] = (float)((double)margin * red[0][0] / (double)kE4M3Max);
-    L.stat[H + h] = (float)((double)margin * red[1][0] / (double)kE4M3Max);
+    L.stat[h] = sk;
+    L.stat[H + h] = sv;
     if (h == 0) reinterpret_cast<int*>(L.stat)[2 * H] = 1;
   }
+  // Requantize the head's valid cache with the new scales (the pages' cache
+  // is bf16 until the calibration and FP8 with the head's scales from then
+  // on): code' = e4m3(code * s_slot / s) with the product and quotient in
+  // double precision, so that every valid slot carries the head's scales
+  // and the attention can apply them per head.  Nothing saturates: every
+  // element is at most amax <= 448 s / margin.  Only this workgroup touches
+  // the head's slots, and every one of its reads above came before the
+  // reduction's barriers.
+  auto requant16 = [](uint4 w, const float* sc, bool per_elem, float s) {
+    float x[16];
+    unpack4_fp8(w.x, x[0], x[1], x[2], x[3]);
+    unpack4_fp8(w.y, x[4], x[5], x[6], x[7]);
+    unpack4_fp8(w.z, x[8], x[9], x[10], x[11]);
+    unpack4_fp8(w.w, x[12], x[13], x[14], x[15]);
+    float q[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      q[e] = __builtin_amdgcn_fmed3f((float)((double)x[e] * (double)sc[per_elem ? e : 0] / (double)s), -kE4M3Max,
+                                     kE4M3Max);
+    uint4 o;
+    uint32_t* ow = &o.x;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ow[c] = pack2_fp8<true>(q[4 * c + 2], q[4 * c + 3], pack2_fp8<false>(q[4 * c], q[4 * c + 1], 0u));
+    return o;
+  };
+  if (sk > 0.f) {
+    for (int idx = (int)threadIdx.x; idx < NP * CH; idx += 256) {
+      const int slot = idx / CH, c = idx % CH;
+      if (!valid(slot)) continue;
+      uint4* p = reinterpret_cast<uint4*>(L.codes_k + ((size_t)h * NP + slot) * D + 16 * c);
+      *p = requant16(*p, L.scale_k + (size_t)h * NP + slot, false, sk);
+    }
+  }
+  if (sv > 0.f) {
+    for (int idx = (int)threadIdx.x; idx < g.n_tiles * D * 4; idx += 256) {
+      const int tile = idx / (D * 4), d = (idx / 4) % D, qtr = idx % 4;
+      const int s0 = kTile * tile + 16 * qtr;
+      bool any = false;
+      float sc[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const bool ok = valid(s0 + e);
+        any |= ok;
+        sc[e] = ok ? L.scale_v[(size_t)h * NP + s0 + e] : 0.f;
+      }
+      if (!any) continue;
+      uint4* p = reinterpret_cast<uint4*>(L.codes_v + (((size_t)h * g.n_tiles + tile) * D + d) * kTile + 16 * qtr);
+      const uint4 old = *p;
+      const uint4 nw = requant16(old, sc, true, sv);
+      // slots outside the valid range keep their bytes
+      uint4 o;
+      const uint32_t* a = &old.x;
+      const uint32_t* b = &nw.x;
+      uint32_t* r = &o.x;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (valid(s0 + 4 * c + e)) m |= 0xFFu << (8 * e);
+        r[c] = (b[c] & m) | (a[c] & ~m);
+      }
+      *p = o;
+    }
+  }
+  __syncthreads();  // every thread's scale reads above are done before the scales change
+  for (int slot = (int)threadIdx.x; slot < N; slot += 256) {
+    if (!valid(slot)) continue;
+    if (sk > 0.f) L.scale_k[(size_t)h * NP + slot] = sk;
+    if (sv > 0.f) L.scale_v[(size_t)h * NP + slot] = sv;
+  }
+  // every valid value scale of the head is now s: the head's bound
+  if (sv > 0.f && (int)threadIdx.x < kSub) L.vmax[h * kSub + threadIdx.x] = __float_as_uint(sv);
 }
 
 hipError_t launch_calibrate(const Geom& g, int layer_lo, int layer_hi, float margin, hipStream_t s) {

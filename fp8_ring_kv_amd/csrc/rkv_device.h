@@ -66,6 +66,14 @@ __host__ __device__ inline LayerPtrs layer_ptrs(const Geom& g, int layer) {
   return p;
 }
 
+// True when head h of a layer is in the pages' static-scale mode with
+// nonzero key and value scales: the calibration has requantized its valid
+// cache, so every valid slot carries the head's scales (a head calibrated at
+// amax 0 keeps the per-(token, head) rule).
+__device__ inline bool static_head(const LayerPtrs& L, int n_heads, int h) {
+  return reinterpret_cast<const int*>(L.stat)[2 * n_heads] != 0 && L.stat[h] > 0.f && L.stat[n_heads + h] > 0.f;
+}
+
 __device__ inline const double* omega_turns(const Geom& g) {
   return reinterpret_cast<const double*>(g.base + g.consts);
 }

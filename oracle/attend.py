@@ -46,6 +46,13 @@ The device kernel's declared numerics, which ``attend_method`` and
   the kernel's running maximum changes which way some codes round, which the
   tolerance covers.
 * The single-term ("fast") mode uses one term for Q and one for P.
+* Static scales (the pages' per-(layer, head) mode, once calibrated: every
+  valid slot of a head carries the head's key scale s_k and value scale
+  s_v): the kernel multiplies the scaled query by s_k before quantizing it,
+  so the products with the key codes come out in log2 units, and feeds
+  x = 7 P (7 = 448 * 2**-6, the headroom) in place of P s_v c; the output is
+  s_v times (x . V codes) / sum x.  (A head whose static scales are 0 keeps
+  the per-token rule.)
 """
 from __future__ import annotations
 
@@ -161,11 +168,20 @@ def attend_emul(st: RingState, q: np.ndarray, q_pos: np.ndarray, q_terms: int = 
     out = np.zeros(qr.shape, dtype=np.float64)
     if slots.size == 0:
         return out
-    qd = quantize_q_terms(qr * softmax_scale_log2(st.head_dim), q_terms)
+    cs = softmax_scale_log2(st.head_dim)
+    qd = quantize_q_terms(qr * cs, q_terms)
     kd = dequant_k(st)[:, slots, :]
     v8 = e4m3.decode(st.codes_v[:, slots, :])  # codes as values
     sv = st.scale_v[:, slots]  # [H, n_valid]
     for h in range(st.n_heads):
+        if static_head(st, h):
+            sk_h, sv_h = st.static_k[h], st.static_v[h]
+            qh = quantize_q_terms(qr[:, h, :] * cs * sk_h, q_terms)
+            s = qh @ e4m3.decode(st.codes_k[h, slots, :]).T  # log2 units
+            p = np.exp2(s - s.max(axis=1, keepdims=True))
+            xq = p_terms_value(7.0 * p, p_terms)  # 7 = 448 * 2**-6
+            out[:, h, :] = sv_h * (xq @ v8[h]) / (7.0 * p.sum(axis=1, keepdims=True))
+            continue
         s = qd[:, h, :] @ kd[h].T  # log2 units
         p = np.exp2(s - s.max(axis=1, keepdims=True))  # <= 1, row max exactly 1
         l = p.sum(axis=1, keepdims=True)
@@ -175,6 +191,14 @@ def attend_emul(st: RingState, q: np.ndarray, q_pos: np.ndarray, q_terms: int = 
         pq = p_terms_value(p * sv[h][None, :] * c, p_terms)
         out[:, h, :] = (pq @ v8[h]) / (c * l)
     return out
+
+
+def static_head(st: RingState, h: int) -> bool:
+    """True when head h is in the pages' static-scale mode with nonzero key
+    and value scales, so every valid slot carries the head's scales (the
+    calibration requantizes the valid cache; later writes and rotations use
+    them)."""
+    return st.static_k is not None and st.static_k[h] > 0 and st.static_v[h] > 0
 
 
 def sigma_v(st: RingState) -> np.ndarray:

@@ -191,10 +191,11 @@ def quantize_static(y: np.ndarray, s_head: np.ndarray, margin: float):
 def calibrate_static(st: RingState, margin: float) -> None:
     """The pages' scale calibration (Appendix G; §4.3 "FP8 at write"): per
     head, s = fp32(margin * amax / 448) with amax the largest magnitude of the
-    dequantized keys (values) over the valid slots, then every later write
-    quantizes with these scales and a reset rotation requantizes the head's
-    keys with its key scale.  A scale of 0 (amax 0: no valid slot, or all
-    zero) leaves that head's keys (values) on per-(token, head) scales."""
+    dequantized keys (values) over the valid slots; the valid cache is
+    requantized with these scales, every later write quantizes with them and
+    a reset rotation requantizes the head's keys with its key scale.  A scale
+    of 0 (amax 0: no valid slot, or all zero) leaves that head's keys
+    (values) on per-(token, head) scales."""
     slots = valid_slots(st)
     amk = np.zeros(st.n_heads)
     amv = np.zeros(st.n_heads)
@@ -203,6 +204,22 @@ def calibrate_static(st: RingState, margin: float) -> None:
         amv = np.max(np.abs(dequant_v(st)[:, slots, :]), axis=(1, 2))
     st.static_k = (margin * amk / e4m3.E4M3_MAX).astype(np.float32).astype(np.float64)
     st.static_v = (margin * amv / e4m3.E4M3_MAX).astype(np.float32).astype(np.float64)
+    # The pages' cache is bf16 until the calibration and FP8 with the head's
+    # scales from then on; this cache is FP8 from the first write, so the
+    # calibration requantizes every valid key and value of a calibrated head
+    # with the head's scale (one more e4m3 rounding of the per-token codes;
+    # nothing saturates: every element is at most amax <= 448 s / margin).
+    # Every valid slot then carries its head's scales, which is what lets the
+    # attention apply them per head.
+    for h in range(st.n_heads):
+        for sh, codes, scales in ((st.static_k[h], st.codes_k, st.scale_k),
+                                  (st.static_v[h], st.codes_v, st.scale_v)):
+            if sh > 0 and slots.size:
+                x = e4m3.decode(codes[h][slots]) * scales[h][slots][:, None]
+                codes[h][slots] = e4m3.encode(x / sh)
+                scales[h][slots] = sh
+        if st.static_v[h] > 0:
+            st.vmax[h] = st.static_v[h]  # every valid value scale is now the head's
 
 
 def dequant_k(st: RingState) -> np.ndarray:

@@ -13,7 +13,7 @@ import fp8_ring_kv_amd as rkv
 from oracle import attend as oatt, ring as oring
 from oracle.bf16 import round_bf16
 from tests.gpu_common import DEV, assert_cache_matches, check_attention, pos_dev, require_gpu, rotate_checked, to_dev
-from workloads import Config, OutlierSpec, Stream, positions
+from workloads import ATTEND, Bf16, Config, OutlierSpec, Stream, positions
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +45,12 @@ def test_static_session_matches_oracle():
     # static scale (2^-22 relative)
     assert np.array_equal(got[1], st.static_v), (got[1], st.static_v)
     assert np.all(np.abs(got[0] - st.static_k) <= st.static_k * 2.0 ** -22), (got[0] - st.static_k, st.static_k)
+    # the calibration requantized the valid cache with the head scales; the
+    # oracle used its own (float64) key scales, the device its own: compare
+    # against an oracle state holding the device's static key scales
+    st.static_k = got[0].copy()
+    st2 = st.copy()
+    assert_cache_matches(cache, 0, st2)
     for c in range(3):  # static writes; the ring wraps and every slot is rewritten
         _, k, v = s.chunk()
         pos = positions(p0, cfg.chunk)
@@ -149,3 +155,60 @@ def test_calibrate_rejects_bad_arguments():
     for m in (0.0, -1.0, 65.0, float("nan")):
         assert L.ring_cache_calibrate_static(vp(cache.handle), 0, m, s) == rkv.RKV_EINVAL, m
     assert "margin" in rkv.rkv_last_error()
+
+
+def test_static_attention_full_size_every_element():
+    """The 757 x 5,788 x 12 workload (ring head at 3,100, 2% outliers x8) after
+    the calibration: the attention takes the static path (s_k in the queries,
+    s_v after the product, no per-slot scales), through the same split-unit
+    merges as the per-token path; every output element against exact fp64
+    attention on the device's cache and the kernel's declared numerics."""
+    cfg = ATTEND
+    cache = rkv.RingCache(1, cfg.n_slots, cfg.n_heads, cfg.head_dim, 757, rkv.RKV_PRECISE, device=DEV)
+    st = oring.RingState(cfg.n_slots, cfg.n_heads, cfg.head_dim)
+    s = Stream(cfg)
+    p0 = 0
+    while p0 < 8888:
+        n = min(757, 8888 - p0)
+        _, k, v = s.chunk(n)
+        cache.write(0, to_dev(k), to_dev(v), pos_dev(positions(p0, n)))
+        oring.write(st, k.f64, v.f64, positions(p0, n))
+        p0 += n
+    cache.calibrate_static(0, 1.5)
+    oring.calibrate_static(st, 1.5)
+    st.static_k = cache.static_scales(0).cpu().numpy().astype(np.float64)[0].copy()
+    q, _, _ = s.chunk(757)
+    qpos = positions(8131, 757)
+    out = cache.attend(0, to_dev(q), pos_dev(qpos)).float().cpu().numpy().astype(np.float64)
+    check_attention("static C2 (all 12 heads x 757 rows)", cache, 0, None, q.f64, qpos, out)
+
+
+def test_static_and_per_token_heads_in_one_layer():
+    """Head 1's keys and values are all zero when the layer is calibrated: its
+    static scales are 0 and it keeps the per-token rule (and the per-token
+    attention) beside head 0's static path; later writes fill both."""
+    cfg = Config("static_mixed", n_heads=2, head_dim=128, n_slots=400, chunk=150, seed=35,
+                 outliers=OutlierSpec(0.02, 8.0))
+    cache = rkv.RingCache(1, cfg.n_slots, 2, 128, 150, device=DEV)
+    st = oring.RingState(cfg.n_slots, 2, 128)
+    s = Stream(cfg)
+    _, k, v = s.chunk()
+    kz = Bf16(k.bits.copy(), k.f64.copy())
+    vz = Bf16(v.bits.copy(), v.f64.copy())
+    for t in (kz, vz):
+        t.bits[:, 1] = 0
+        t.f64[:, 1] = 0.0
+    cache.write(0, to_dev(kz), to_dev(vz), pos_dev(positions(0, 150)))
+    oring.write(st, kz.f64, vz.f64, positions(0, 150))
+    cache.calibrate_static(0, 1.5)
+    oring.calibrate_static(st, 1.5)
+    stat = cache.static_scales(0).cpu().numpy()
+    assert stat[0, 0] > 0 and stat[1, 0] > 0 and stat[0, 1] == 0 and stat[1, 1] == 0
+    st.static_k = stat[0].astype(np.float64).copy()
+    for c in (1, 2):
+        q, k, v = s.chunk()
+        pos = positions(150 * c, 150)
+        cache.write(0, to_dev(k), to_dev(v), pos_dev(pos))
+        oring.write(st, k.f64, v.f64, pos)
+        out = cache.attend(0, to_dev(q), pos_dev(pos)).float().cpu().numpy().astype(np.float64)
+        check_attention(f"mixed static/per-token heads, chunk {c}", cache, 0, st, q.f64, pos, out)

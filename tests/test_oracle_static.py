@@ -20,10 +20,31 @@ def test_calibration_is_margin_times_largest_per_token_scale():
     """Per-token margin-1 rows put their amax element on code 448 exactly, so the
     cache's amax is 448 * max scale and the static scale is fp32(1.5 * max scale)."""
     st, _ = session()
+    sk, sv = st.scale_k.copy(), st.scale_v.copy()
     ring.calibrate_static(st, 1.5)
     for h in range(st.n_heads):
-        assert st.static_k[h] == np.float32(1.5 * st.scale_k[h].max())
-        assert st.static_v[h] == np.float32(1.5 * st.scale_v[h].max())
+        assert st.static_k[h] == np.float32(1.5 * sk[h].max())
+        assert st.static_v[h] == np.float32(1.5 * sv[h].max())
+
+
+def test_calibration_requantizes_the_valid_cache_with_the_head_scales():
+    """After the calibration every valid slot carries its head's scales, each
+    element is the pre-calibration value rounded once to the head's e4m3 grid
+    (within half an ulp of it), nothing saturates (every value is at most
+    amax = 448 s / 1.5), and the value-scale bound is the head's scale."""
+    st, _ = session()
+    before_k, before_v = ring.dequant_k(st), ring.dequant_v(st)
+    ring.calibrate_static(st, 1.5)
+    slots = ring.valid_slots(st)
+    for before, codes, scales, stat in ((before_k, st.codes_k, st.scale_k, st.static_k),
+                                        (before_v, st.codes_v, st.scale_v, st.static_v)):
+        assert np.all(scales[:, slots] == stat[:, None])
+        c = codes[:, slots]
+        got = e4m3.decode(c) * stat[:, None, None]
+        half = e4m3.ulp_at(c) * stat[:, None, None] / 2
+        assert np.all(np.abs(got - before[:, slots]) <= half * (1 + 1e-12))
+        assert np.max(np.abs(e4m3.decode(c))) <= 448 / 1.5 + 16  # at most one step above amax/s
+    assert np.array_equal(st.vmax, st.static_v)
 
 
 def test_static_write_saturates_beyond_the_scale():
@@ -148,3 +169,35 @@ def test_zero_key_head_static_values_only():
     # head 1's keys: per-token rule, amax maps to 448
     assert np.all(np.max(np.abs(e4m3.decode(st.codes_k[1, new])), axis=-1) == 448)
     assert np.all(st.scale_k[1, new] == np.float32(np.max(np.abs(rope(k2, new)[:, 1]), axis=-1) / 448))
+
+
+def test_static_attention_emulation_equals_the_per_token_formula_on_calibrated_heads():
+    """On a calibrated cache every valid slot carries its head's scales, so the
+    kernel's static attention (s_k folded into the queries, x = 7 P, s_v
+    after the product) is the per-token emulation with s_v = vmax: the two
+    differ only where folding s_k into Q moves a query code and in the last
+    bits (fp32 c against the exact 7), and both sit within the contract of
+    exact attention; heads with a zero static scale take the per-token rule."""
+    from oracle import attend
+    from oracle.bf16 import round_bf16
+    st, rng = session(n_slots=200, chunks=10, seed=5)
+    ring.calibrate_static(st, 1.5)
+    q = rng.standard_normal((40, 2, 64))
+    pos = np.arange(100, 140)
+    stat = attend.attend_emul(st, q, pos)
+    plain = st.copy()
+    plain.static_k = plain.static_v = None  # same cache, per-token numerics
+    tok = attend.attend_emul(plain, q, pos)
+    ex = attend.attend_exact(st, q, pos)
+    sig = np.maximum(1, attend.sigma_v(st))[None]
+    assert np.max(np.abs(stat - tok) / sig) < 5e-3
+    for out in (stat, tok):
+        e = np.abs(round_bf16(out) - ex) / sig
+        assert e.max() < 2e-2 and e.mean() < 2e-3
+    # one value code at 448 (the row max of a one-slot cache): x = 7 exactly
+    one = ring.RingState(16, 1, 64)
+    ring.write(one, rng.standard_normal((1, 1, 64)), rng.standard_normal((1, 1, 64)), [3])
+    ring.calibrate_static(one, 1.5)
+    got = attend.attend_emul(one, rng.standard_normal((3, 1, 64)), np.arange(3))
+    want = ring.dequant_v(one)[:, 0, :]
+    assert np.max(np.abs(got - want[None])) <= 1e-15 * np.max(np.abs(want))
