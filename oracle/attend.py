@@ -61,7 +61,7 @@ import math
 import numpy as np
 
 from . import e4m3
-from .ring import RingState, dequant_k, dequant_v, valid_slots
+from .ring import RingState, dequant_k, dequant_v, rope_keys, valid_slots
 from .rope import rope
 
 
@@ -88,7 +88,7 @@ def _prepare(st: RingState, q: np.ndarray, q_pos: np.ndarray):
     if q.ndim != 3 or q.shape[1] != st.n_heads or q.shape[2] != st.head_dim:
         raise ValueError("attend: q must be [n_q, H, D]")
     slots = valid_slots(st)
-    qr = rope(q, q_pos, st.rope_base)  # [n_q, H, D]
+    qr = rope_keys(st, q, q_pos)  # [n_q, H, D], the state's RoPE (1-D or 3-D)
     return qr, slots
 
 

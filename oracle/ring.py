@@ -49,7 +49,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from . import e4m3
-from .rope import delta_angles, rope, rotate_pairs
+from .rope import delta_angles, delta_angles3d, rope, rope3d, rotate_pairs
 
 
 @dataclass
@@ -71,11 +71,23 @@ class RingState:
     # (float64 holding fp32 values); None: per-(token, head) amax scales
     static_k: np.ndarray = field(default=None)
     static_v: np.ndarray = field(default=None)
+    # global (sink) slots after the ring: canonical slots n_slots ..
+    # n_slots + n_global - 1, written at explicit indices, never rotated;
+    # g_valid = 1 + the highest global index written since the reset
+    n_global: int = 0
+    g_valid: int = 0
+    # 3-D RoPE: (n_t, n_y, n_x) pairs per band (rope.band_table); None: 1-D
+    # positions.  With bands, slot_pos holds t and slot_yx (y, x).
+    bands: tuple = None
+    slot_yx: np.ndarray = field(default=None)
 
     def __post_init__(self):
-        n, h, d = self.n_slots, self.n_heads, self.head_dim
+        h, d = self.n_heads, self.head_dim
+        n = self.n_slots + self.n_global
         if self.slot_pos is None:
             self.slot_pos = np.zeros(n, dtype=np.int64)
+        if self.slot_yx is None:
+            self.slot_yx = np.zeros((n, 2), dtype=np.int64)
         if self.codes_k is None:
             self.codes_k = np.zeros((h, n, d), dtype=np.uint8)
         if self.codes_v is None:
@@ -93,13 +105,37 @@ class RingState:
                          self.codes_v.copy(), self.scale_k.copy(), self.scale_v.copy(),
                          self.vmax.copy(),
                          None if self.static_k is None else self.static_k.copy(),
-                         None if self.static_v is None else self.static_v.copy())
+                         None if self.static_v is None else self.static_v.copy(),
+                         self.n_global, self.g_valid, self.bands, self.slot_yx.copy())
+
+
+def ring_valid_slots(st: RingState) -> np.ndarray:
+    """Ring slots of the valid range, oldest first: (head - n_valid + k) mod N."""
+    k = np.arange(st.n_valid, dtype=np.int64)
+    return (st.head - st.n_valid + k) % st.n_slots
 
 
 def valid_slots(st: RingState) -> np.ndarray:
-    """Physical slots of the valid range, oldest first: (head - n_valid + k) mod N."""
-    k = np.arange(st.n_valid, dtype=np.int64)
-    return (st.head - st.n_valid + k) % st.n_slots
+    """Every slot the attention reads: the ring's valid range, oldest first,
+    then the global slots written since the reset."""
+    return np.concatenate([ring_valid_slots(st), st.n_slots + np.arange(st.g_valid, dtype=np.int64)])
+
+
+def rope_keys(st: RingState, x: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    """RoPE of [n, H, D] rows at the state's position kind: int [n] (1-D) or
+    [n, 3] = (t, y, x) with the state's bands."""
+    if st.bands is None:
+        return rope(x, pos, st.rope_base)
+    return rope3d(x, pos, st.bands, st.rope_base)
+
+
+def _set_positions(st: RingState, slots: np.ndarray, pos: np.ndarray) -> None:
+    pos = np.asarray(pos, dtype=np.int64)
+    if st.bands is None:
+        st.slot_pos[slots] = pos
+    else:
+        st.slot_pos[slots] = pos[:, 0]
+        st.slot_yx[slots] = pos[:, 1:3]
 
 
 def write_slots(st: RingState, n: int) -> np.ndarray:
@@ -108,49 +144,75 @@ def write_slots(st: RingState, n: int) -> np.ndarray:
 
 
 def write(st: RingState, k: np.ndarray, v: np.ndarray, pos: np.ndarray) -> None:
-    """Write n new tokens: RoPE on K at their positions, FP8 quantize K and V.
+    """Write n new tokens into the ring: RoPE on K at their positions, FP8
+    quantize K and V.
 
-    k, v: [n, H, D] float64 (bf16 values); pos: [n] integer positions.
-    Token i goes to slot (head + i) mod N and the slot remembers pos[i].
-    Then head <- (head + n) mod N and n_valid <- min(n_valid + n, N).
+    k, v: [n, H, D] float64 (bf16 values); pos: [n] integer positions (1-D)
+    or [n, 3] (t, y, x) with 3-D RoPE.  Token i goes to slot (head + i) mod N
+    and the slot remembers its position.  Then head <- (head + n) mod N and
+    n_valid <- min(n_valid + n, N).
     """
+    n = np.asarray(k).shape[0]
+    if not (0 < n <= st.n_slots):
+        raise ValueError("write: n must be in 1..n_slots")
+    slots = write_slots(st, n)
+    _store(st, slots, k, v, pos)
+    st.head = int((st.head + n) % st.n_slots)
+    st.n_valid = int(min(st.n_valid + n, st.n_slots))
+
+
+def write_global(st: RingState, first: int, k: np.ndarray, v: np.ndarray, pos: np.ndarray) -> None:
+    """Write n tokens into the global (sink) slots first .. first + n - 1 (the
+    pages' global tokens, written once per session, never rotated): RoPE at
+    their positions and FP8 quantization as in the ring write.  g_valid
+    becomes max(g_valid, first + n)."""
+    n = np.asarray(k).shape[0]
+    if not (0 < n and 0 <= first and first + n <= st.n_global):
+        raise ValueError("write_global: slots out of range")
+    slots = st.n_slots + first + np.arange(n, dtype=np.int64)
+    _store(st, slots, k, v, pos)
+    st.g_valid = int(max(st.g_valid, first + n))
+
+
+def _store(st: RingState, slots: np.ndarray, k: np.ndarray, v: np.ndarray, pos: np.ndarray) -> None:
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     pos = np.asarray(pos, dtype=np.int64)
     n = k.shape[0]
-    if not (0 < n <= st.n_slots):
-        raise ValueError("write: n must be in 1..n_slots")
-    if k.shape != (n, st.n_heads, st.head_dim) or v.shape != k.shape or pos.shape != (n,):
+    want_pos = (n,) if st.bands is None else (n, 3)
+    if k.shape != (n, st.n_heads, st.head_dim) or v.shape != k.shape or pos.shape != want_pos:
         raise ValueError("write: shape mismatch")
-    k_rot = rope(k, pos, st.rope_base)  # [n, H, D]
+    k_rot = rope_keys(st, k, pos)  # [n, H, D]
     if st.static_k is None:
         ck, sk = e4m3.quantize_rows(k_rot, st.margin)  # [n, H, D], [n, H]
         cv, sv = e4m3.quantize_rows(v, st.margin)
     else:
         ck, sk = quantize_static(k_rot, st.static_k, st.margin)
         cv, sv = quantize_static(v, st.static_v, st.margin)
-    slots = write_slots(st, n)
     st.codes_k[:, slots, :] = np.transpose(ck, (1, 0, 2))
     st.codes_v[:, slots, :] = np.transpose(cv, (1, 0, 2))
     st.scale_k[:, slots] = sk.T
     st.scale_v[:, slots] = sv.T
-    st.slot_pos[slots] = pos
+    _set_positions(st, slots, pos)
     st.vmax = np.maximum(st.vmax, sv.max(axis=0))
-    st.head = int((st.head + n) % st.n_slots)
-    st.n_valid = int(min(st.n_valid + n, st.n_slots))
 
 
 def rotate(st: RingState, delta: int) -> None:
-    """Delta rotation at a position reset, in place, on every valid slot.
+    """Delta rotation at a position reset, in place, on every valid ring slot.
 
-    Each valid key (every head) is dequantized with its scale, each pair j is
-    rotated by phi_j = delta * omega_j, a new scale is taken from the rotated
-    key's amax, and the key is requantized.  slot_pos += delta.  V untouched.
+    Each valid ring key (every head) is dequantized with its scale, each pair
+    j is rotated by phi_j = delta * omega_j (with 3-D RoPE only the temporal
+    pairs; the spatial ones keep their values), a new scale is taken from the
+    rotated key's amax, and the key is requantized.  slot_pos (the temporal
+    position) += delta.  V untouched; global slots untouched.
     """
-    slots = valid_slots(st)
+    slots = ring_valid_slots(st)  # global slots never move
     if slots.size == 0:
         return
-    c, s = delta_angles(st.head_dim, delta, st.rope_base)
+    if st.bands is None:
+        c, s = delta_angles(st.head_dim, delta, st.rope_base)
+    else:  # only the temporal band turns; spatial pairs keep their values
+        c, s = delta_angles3d(st.head_dim, st.bands, delta, st.rope_base)
     x = e4m3.decode(st.codes_k[:, slots, :]) * st.scale_k[:, slots][..., None]
     y = rotate_pairs(x, c, s)
     ck, sk = e4m3.quantize_rows(y, st.margin)
@@ -167,11 +229,14 @@ def rotate(st: RingState, delta: int) -> None:
 
 
 def reset(st: RingState) -> None:
-    """Session reset: empty ring (head 0, no valid slots, positions 0, vmax 0),
-    back to per-(token, head) scales until the next calibration."""
+    """Session reset: empty ring and no global slots (head 0, no valid slots,
+    positions 0, vmax 0), back to per-(token, head) scales until the next
+    calibration."""
     st.head = 0
     st.n_valid = 0
+    st.g_valid = 0
     st.slot_pos[:] = 0
+    st.slot_yx[:] = 0
     st.vmax[:] = 0
     st.static_k = st.static_v = None
 

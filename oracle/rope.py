@@ -55,3 +55,49 @@ def delta_angles(head_dim: int, delta: int, base: float = 10000.0):
     """(cos, sin) of phi_j = delta * omega_j, float64, shape [D/2]."""
     phi = np.float64(delta) * omega(head_dim, base)
     return np.cos(phi), np.sin(phi)
+
+
+# ---- 3-D RoPE (global slots and banded positions) ---------------------------
+#
+# The pages' model places each token at a temporal index t (the latent frame)
+# and spatial coordinates; the temporal angle of frequency j is
+# theta_j(t) = omega_j (a t + b), spatial angles and global tokens do not
+# depend on the window, and a reset rotates only the temporal frequencies
+# (§4.2, Appendix G).  The pages do not give the band layout.  Readings taken
+# here: the D/2 interleaved pairs of a head form three contiguous bands of
+# n_t, n_y and n_x pairs (temporal, height, width; the caller chooses the
+# counts, n_t + n_y + n_x = D/2); each band is a RoPE of its own dimension
+# 2 n_b, omega_{b,j} = base**(-j / n_b) for its j-th pair, at the token's
+# coordinate on that axis; a = 1, b = 0.  With n_y = n_x = 0 this is the 1-D
+# RoPE above (omega_j = base**(-2j/D) at position t).
+
+
+def band_table(head_dim: int, bands, base: float = 10000.0):
+    """Per pair j: (axis index 0 = t, 1 = y, 2 = x; omega) as two arrays [D/2]."""
+    n_t, n_y, n_x = (int(b) for b in bands)
+    if n_t + n_y + n_x != head_dim // 2 or min(n_t, n_y, n_x) < 0:
+        raise ValueError("bands must be non-negative pair counts summing to head_dim / 2")
+    axis, om = [], []
+    for a, nb in enumerate((n_t, n_y, n_x)):
+        j = np.arange(nb, dtype=np.float64)
+        axis.append(np.full(nb, a, dtype=np.int64))
+        om.append(np.power(np.float64(base), -j / nb) if nb else j)
+    return np.concatenate(axis), np.concatenate(om)
+
+
+def rope3d(x: np.ndarray, pos3: np.ndarray, bands, base: float = 10000.0) -> np.ndarray:
+    """RoPE of tokens x [n, H, D] at coordinates pos3 [n, 3] = (t, y, x), banded."""
+    x = np.asarray(x, dtype=np.float64)
+    n, _, d = x.shape
+    axis, om = band_table(d, bands, base)
+    p = np.asarray(pos3, dtype=np.float64).reshape(n, 3)
+    theta = p[:, axis] * om[None, :]  # [n, D/2]
+    return rotate_pairs(x, np.cos(theta)[:, None, :], np.sin(theta)[:, None, :])
+
+
+def delta_angles3d(head_dim: int, bands, delta: int, base: float = 10000.0):
+    """(cos, sin) [D/2] of a reset by delta temporal positions: temporal pairs
+    rotate by delta * omega_j, spatial pairs not at all (cos 1, sin 0)."""
+    axis, om = band_table(head_dim, bands, base)
+    phi = np.where(axis == 0, np.float64(delta) * om, 0.0)
+    return np.cos(phi), np.sin(phi)
