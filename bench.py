@@ -399,6 +399,22 @@ def main():
         comp["stress_attend_TFLOPs"] = STRESS_FLOP / comp["stress_attend_us"] / 1e6
         assert torch.isfinite(outs.float()).all()
         del st, ks, vs, qs, outs
+        # the pages' layout: 1,246 global slots + a 4,542-slot ring of six
+        # 757-token latents with 3-D RoPE (22/21/21 pairs); one attention call
+        # of 757 queries over all 5,788 slots (the same work as the ring-only
+        # workload) and one latent write
+        from workloads import PAGES_LAYOUT, frame_positions
+        pg = rkv.RingCache(1, PAGES_LAYOUT.n_slots, H, D, CHUNK, prec, device=dev,
+                           n_global=PAGES_LAYOUT.n_global, rope_bands=PAGES_LAYOUT.bands)
+        kg = torch.randn(PAGES_LAYOUT.n_global, H, D, generator=gen, device=dev).to(torch.bfloat16)
+        pg.write_global(0, 0, kg, kg, torch.from_numpy(frame_positions(-1, PAGES_LAYOUT.n_global, 36)).to(dev))
+        fpos = [torch.from_numpy(frame_positions(t, CHUNK, 28)).to(dev) for t in range(8)]
+        for t in range(8):
+            q, k, v = pool[t]
+            pg.write(0, k, v, fpos[t])
+        comp["pages_layout_attend_us"] = 1e3 * timed(lambda: pg.attend(0, q0, fpos[7], out), r, stream)
+        comp["pages_layout_write_us"] = 1e3 * timed(lambda: pg.write(0, k0, v0, fpos[7]), r, stream)
+        del pg, kg
         # one write of a whole ring's worth of tokens (5,788 x 12 heads, 54 MB
         # moved): the write kernel with enough work to approach bandwidth
         fr = rkv.RingCache(1, N, H, D, CHUNK, prec, device=dev)

@@ -22,7 +22,8 @@ __all__ = [
     "RKV_OK", "RKV_EINVAL", "RKV_EHIP", "RKV_PRECISE", "RKV_FAST",
     "rkv_params", "rkv_layout", "RkvError", "lib", "lib_path",
     "ring_cache_bytes", "ring_cache_create", "ring_cache_destroy", "ring_cache_reset",
-    "ring_cache_layout", "cache_write_rope_fp8", "cache_delta_rotate", "cache_attend", "cache_attend_noalloc",
+    "ring_cache_layout", "cache_write_rope_fp8", "cache_write_global", "cache_delta_rotate", "cache_attend",
+    "cache_attend_noalloc",
     "cache_write_attend", "ring_cache_set_qk_norm", "ring_cache_calibrate_static",
     "rkv_last_error", "RingCache",
 ]
@@ -49,6 +50,8 @@ class rkv_params(ctypes.Structure):
         ("scale_margin", ctypes.c_float),
         ("attn_workgroups", ctypes.c_int32),
         ("attn_merge_wait_us", ctypes.c_int32),
+        ("n_global", ctypes.c_int32),
+        ("rope_bands", ctypes.c_int32 * 3),
     ]
 
 
@@ -63,6 +66,9 @@ class rkv_layout(ctypes.Structure):
         ("vmax", ctypes.c_size_t),
         ("layer_bytes", ctypes.c_size_t),
         ("n_slots_padded", ctypes.c_int32),
+        ("slot_yx", ctypes.c_size_t),
+        ("n_global", ctypes.c_int32),
+        ("global_first_slot", ctypes.c_int32),
     ]
 
 
@@ -101,6 +107,8 @@ def lib() -> ctypes.CDLL:
     L.cache_delta_rotate.restype = ctypes.c_int
     L.cache_attend.argtypes = [VP, I32, VP, VP, I32, VP, VP]
     L.cache_attend.restype = ctypes.c_int
+    L.cache_write_global.argtypes = [VP, I32, I32, VP, VP, VP, I32, VP]
+    L.cache_write_global.restype = ctypes.c_int
     L.cache_attend_noalloc.argtypes = [VP, I32, VP, VP, I32, VP, VP]
     L.cache_attend_noalloc.restype = ctypes.c_int
     L.cache_write_attend.argtypes = [VP, I32, VP, VP, VP, I32, VP, VP, I32, VP, VP]
@@ -157,6 +165,13 @@ def cache_write_rope_fp8(handle: int, layer: int, k: int, v: int, pos: int, n: i
                                     ctypes.c_void_p(v), ctypes.c_void_p(pos), n, ctypes.c_void_p(stream))
     if rc != RKV_OK:
         raise RkvError(rc, "cache_write_rope_fp8")
+
+
+def cache_write_global(handle: int, layer: int, first: int, k: int, v: int, pos: int, n: int, stream: int) -> None:
+    rc = lib().cache_write_global(ctypes.c_void_p(handle), layer, first, ctypes.c_void_p(k), ctypes.c_void_p(v),
+                                  ctypes.c_void_p(pos), n, ctypes.c_void_p(stream))
+    if rc != RKV_OK:
+        raise RkvError(rc, "cache_write_global")
 
 
 def cache_delta_rotate(handle: int, layer: int, delta: int, stream: int) -> None:
@@ -223,9 +238,13 @@ class RingCache:
     def __init__(self, n_layers: int, n_slots: int, n_heads: int, head_dim: int, max_queries: int,
                  precision: int = RKV_PRECISE, rope_base: float = 10000.0, scale_margin: float = 1.0,
                  device: str | torch.device = "cuda", stream=None, attn_workgroups: int = 0,
-                 attn_merge_wait_us: int = -1):
+                 attn_merge_wait_us: int = -1, n_global: int = 0, rope_bands=(0, 0, 0)):
         self.params = rkv_params(n_layers, n_slots, n_heads, head_dim, max_queries, precision,
-                                 rope_base, scale_margin, attn_workgroups, attn_merge_wait_us)
+                                 rope_base, scale_margin, attn_workgroups, attn_merge_wait_us, n_global,
+                                 (ctypes.c_int32 * 3)(*rope_bands))
+        self.n_global = n_global
+        self.rope_bands = tuple(int(b) for b in rope_bands)
+        self.pos_width = 3 if any(rope_bands) else 1
         nbytes = ring_cache_bytes(self.params)
         if nbytes == 0:
             raise RkvError(RKV_EINVAL, "ring_cache_bytes")
@@ -248,15 +267,29 @@ class RingCache:
         except Exception:
             pass
 
+    def _pos_shape(self, n: int):
+        return (n,) if self.pos_width == 1 else (n, 3)
+
     # -- hot path --
     def write(self, layer: int, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor, stream=None):
         n = k.shape[0]
         shape = (n, self.n_heads, self.head_dim)
         _check(k, torch.bfloat16, shape, "k")
         _check(v, torch.bfloat16, shape, "v")
-        _check(pos, torch.int32, (n,), "pos")
+        _check(pos, torch.int32, self._pos_shape(n), "pos")
         cache_write_rope_fp8(self.handle, layer, k.data_ptr(), v.data_ptr(), pos.data_ptr(), n,
                              _stream_handle(stream))
+
+    def write_global(self, layer: int, first: int, k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor,
+                     stream=None):
+        """Global (sink) slots first .. first + n - 1 of `layer`."""
+        n = k.shape[0]
+        shape = (n, self.n_heads, self.head_dim)
+        _check(k, torch.bfloat16, shape, "k")
+        _check(v, torch.bfloat16, shape, "v")
+        _check(pos, torch.int32, self._pos_shape(n), "pos")
+        cache_write_global(self.handle, layer, first, k.data_ptr(), v.data_ptr(), pos.data_ptr(), n,
+                           _stream_handle(stream))
 
     def set_qk_norm(self, layer: int, wq: torch.Tensor | None, wk: torch.Tensor | None, eps: float = 1e-6,
                     stream=None):
@@ -296,7 +329,7 @@ class RingCache:
         n_q = q.shape[0]
         shape = (n_q, self.n_heads, self.head_dim)
         _check(q, torch.bfloat16, shape, "q")
-        _check(q_pos, torch.int32, (n_q,), "q_pos")
+        _check(q_pos, torch.int32, self._pos_shape(n_q), "q_pos")
         if out is None:
             out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
         _check(out, torch.bfloat16, shape, "out")
@@ -310,10 +343,10 @@ class RingCache:
         n, n_q = k.shape[0], q.shape[0]
         _check(k, torch.bfloat16, (n, self.n_heads, self.head_dim), "k")
         _check(v, torch.bfloat16, (n, self.n_heads, self.head_dim), "v")
-        _check(pos, torch.int32, (n,), "pos")
+        _check(pos, torch.int32, self._pos_shape(n), "pos")
         shape = (n_q, self.n_heads, self.head_dim)
         _check(q, torch.bfloat16, shape, "q")
-        _check(q_pos, torch.int32, (n_q,), "q_pos")
+        _check(q_pos, torch.int32, self._pos_shape(n_q), "q_pos")
         if out is None:
             out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
         _check(out, torch.bfloat16, shape, "out")
@@ -332,8 +365,8 @@ class RingCache:
         return self.buf[off:off + nbytes].view(dtype)
 
     def state(self, layer: int) -> torch.Tensor:
-        """(head, n_valid, ...) int32 on device (entries past the first two are
-        counters internal to the write kernel)."""
+        """(head, n_valid, ticket counter, g_valid) int32 on device (the third is
+        internal to the write kernel, zero between calls)."""
         lay = self.layout(layer)
         return self._view(lay.state, 16, torch.int32)
 
@@ -342,30 +375,46 @@ class RingCache:
         int32 on device; zero between calls."""
         lay = self.layout(layer)
         region = self._view(lay.state, 4 * 64 * 9, torch.int32)
-        return torch.cat([region[2:4], region[64::64]])
+        return torch.cat([region[2:3], region[64::64]])
 
     def vmax(self, layer: int) -> torch.Tensor:
         """[H] float32: largest value scale written to each head since the reset."""
         lay = self.layout(layer)
         return self._view(lay.vmax, 4 * 8 * self.n_heads, torch.float32).view(self.n_heads, 8).amax(dim=1)
 
+    def _canon(self, t: torch.Tensor, lay: rkv_layout) -> torch.Tensor:
+        """Slot axis (dim 1, or 0 for 1-D) in canonical order: the ring's slots,
+        then the global slots."""
+        g0, ng = lay.global_first_slot, lay.n_global
+        if t.dim() == 1:
+            return torch.cat([t[: self.n_slots], t[g0:g0 + ng]]) if ng else t[: self.n_slots]
+        return torch.cat([t[:, : self.n_slots], t[:, g0:g0 + ng]], dim=1) if ng else t[:, : self.n_slots]
+
     def slot_pos(self, layer: int) -> torch.Tensor:
+        """[N + n_global] int32: each slot's position (3-D RoPE: t), ring then globals."""
         lay = self.layout(layer)
-        return self._view(lay.slot_pos, 4 * lay.n_slots_padded, torch.int32)[: self.n_slots]
+        return self._canon(self._view(lay.slot_pos, 4 * lay.n_slots_padded, torch.int32), lay)
+
+    def slot_yx(self, layer: int) -> torch.Tensor:
+        """[N + n_global][2] int32: spatial coordinates (y, x) of each slot (3-D RoPE)."""
+        lay = self.layout(layer)
+        yx = self._view(lay.slot_yx, 8 * lay.n_slots_padded, torch.int32).view(2, lay.n_slots_padded)
+        return self._canon(yx, lay).t()
 
     def scales(self, layer: int):
-        """(scale_k, scale_v) as [H][N] float32 device views."""
+        """(scale_k, scale_v) as [H][N + n_global] float32 tensors (ring, then globals)."""
         lay = self.layout(layer)
         n = self.n_heads * lay.n_slots_padded * 4
         sk = self._view(lay.scale_k, n, torch.float32).view(self.n_heads, lay.n_slots_padded)
         sv = self._view(lay.scale_v, n, torch.float32).view(self.n_heads, lay.n_slots_padded)
-        return sk[:, : self.n_slots], sv[:, : self.n_slots]
+        return self._canon(sk, lay), self._canon(sv, lay)
 
     def codes(self, layer: int):
-        """(codes_k, codes_v) as [H][N][D] uint8 tensors in slot order (V de-tiled)."""
+        """(codes_k, codes_v) as [H][N + n_global][D] uint8 tensors in canonical
+        slot order (V de-tiled)."""
         lay = self.layout(layer)
         H, D, NP = self.n_heads, self.head_dim, lay.n_slots_padded
-        ck = self._view(lay.codes_k, H * NP * D, torch.uint8).view(H, NP, D)[:, : self.n_slots]
+        ck = self._view(lay.codes_k, H * NP * D, torch.uint8).view(H, NP, D)
         cv = self._view(lay.codes_v, H * NP * D, torch.uint8).view(H, NP // 64, D, 64)
-        cv = cv.permute(0, 1, 3, 2).reshape(H, NP, D)[:, : self.n_slots]
-        return ck, cv
+        cv = cv.permute(0, 1, 3, 2).reshape(H, NP, D)
+        return self._canon(ck, lay), self._canon(cv, lay)

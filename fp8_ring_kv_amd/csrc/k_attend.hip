@@ -533,8 +533,9 @@ __device__ inline void q_prep_body(const QPrepArgs& A, int block) {
   const bool active = qi < A.n_q;
   const int qr = active ? qi : A.n_q - 1;
   const uint4* qp = A.q + ((size_t)qr * H + h) * (D / 8) + part * (EPT / 8);
-  const int32_t p = A.q_pos[qr];
-  const double* turns = omega_turns(A.g) + part * (EPT / 2);
+  const int32_t* pq = A.q_pos + (size_t)qr * A.g.pos_stride;  // (t) or (t, y, x)
+  const int j0 = part * (EPT / 2);                             // this thread's first RoPE pair
+  const double* turns = omega_turns(A.g) + j0;
   float xs[EPT];
 #pragma unroll
   for (int c = 0; c < EPT / 8; ++c) {
@@ -573,7 +574,7 @@ __device__ inline void q_prep_body(const QPrepArgs& A, int block) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       float cs, sn;
-      rope_cs(p, turns[4 * c + m], cs, sn);
+      rope_cs(pair_coord(A.g, pq, j0 + 4 * c + m), turns[4 * c + m], cs, sn);
       const float x0 = xs[8 * c + 2 * m], x1 = xs[8 * c + 2 * m + 1];
       y[8 * c + 2 * m] = (x0 * cs - x1 * sn) * qsc;
       y[8 * c + 2 * m + 1] = (x0 * sn + x1 * cs) * qsc;
@@ -858,16 +859,19 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
   const int u_pre = G % U == 0 ? gi / (G / U) : -1;
   if (u_pre >= 0) load_q(u_pre);
 
-  const int head = L.state[0], nv = L.state[1];
+  const int head = L.state[0], nv = L.state[1], gv = L.state[3];
   int a = head - nv;
   if (a < 0) a += N;
+  const int NTR = g.n_ring_tiles;
   const int T0 = a / kTile;  // tile of the oldest valid slot
-  int count = 0;             // tiles holding valid slots, in cyclic order from T0
+  int count_r = 0;           // ring tiles holding valid slots, in cyclic order from T0
   if (nv > 0) {
     const int e = a + nv - 1;
-    count = e < N ? e / kTile - T0 + 1 : (NT - T0) + (e - N) / kTile + 1;
-    if (count > NT) count = NT;
+    count_r = e < N ? e / kTile - T0 + 1 : (NTR - T0) + (e - N) / kTile + 1;
+    if (count_r > NTR) count_r = NTR;
   }
+  // then the tiles of the global slots below g_valid
+  const int count = count_r + (gv + kTile - 1) / kTile;
 
   if (count == 0) {  // empty cache: every output row is zero
     for (int u = gi; u < U; u += G) {
@@ -888,7 +892,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
   constexpr int C = TileLds<D>::COPIES;
   const long long W = (long long)U * count;
   const long long r_lo = (long long)gi * W / G, r_hi = (long long)(gi + 1) * W / G;
-  auto tile_of = [&](int kk) { const int T = T0 + kk; return T >= NT ? T - NT : T; };
+  auto tile_of = [&](int kk) {
+    if (kk >= count_r) return NTR + (kk - count_r);  // global tiles follow the ring's
+    const int T = T0 + kk;
+    return T >= NTR ? T - NTR : T;
+  };
   int fin[2], nfin = 0;  // split units with output blocks for this workgroup to merge,
   int fin_blocks[2];     // ... those blocks, with kLastArrival if it was their last arrival
 
@@ -951,16 +959,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
         read_k<D>(kf, lb, off);
         qk<D, QT>(sacc, kf, qf, qs);
         read_v<D>(vf, lb, off);
-        // Only the first and last tiles of the valid range and the ring's last
-        // tile (pad slots) can hold invalid slots: the others skip the mask.
-        const int T = tile_of(t_lo + j);
+        // Only the first and last tiles of the ring's valid range, the
+        // ring's last tile (pad slots) and the last global tile can hold
+        // invalid slots: the others skip the mask.
+        const int kk = t_lo + j;
+        const int T = tile_of(kk);
         unsigned long long mask = ~0ull;
-        if (t_lo + j == 0 || t_lo + j == count - 1 || T == NT - 1) {
-          const int sl = T * kTile + lane;
-          int rel = sl - a;
-          if (rel < 0) rel += N;
-          mask = __ballot(sl < N && rel < nv);
-        }
+        if (kk == 0 || kk == count_r - 1 || kk == count - 1 || T == NTR - 1)
+          mask = __ballot(slot_valid(g, T * kTile + lane, a, nv, gv));
         softmax_pv<D, TERMS, ST>(sacc, vf, st, mask, l2c, lane, lb + off.sk4);
       }
     };

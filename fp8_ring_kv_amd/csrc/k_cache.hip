@@ -51,11 +51,15 @@ hipError_t launch_init_consts(const Geom& g, const double* turns, int n, hipStre
 }
 
 // ---------------------------------------------------------------------------
-// Session reset: head = n_valid = 0 and every slot position = 0.
+// Session reset: head = n_valid = g_valid = 0 and every slot position = 0.
 __global__ void reset_kernel(Geom g, int layer_lo) {
   const LayerPtrs L = layer_ptrs(g, layer_lo + (int)blockIdx.y);
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < g.n_pad) L.slot_pos[i] = 0;
+  if (i < g.n_pad) {
+    L.slot_pos[i] = 0;
+    L.slot_yx[i] = 0;
+    L.slot_yx[g.n_pad + i] = 0;
+  }
   if (blockIdx.x == 0)
     for (int j = (int)threadIdx.x; j < kStateRegionInts; j += (int)blockDim.x) L.state[j] = 0;
   if (blockIdx.x == 0)
@@ -98,14 +102,10 @@ __global__ __launch_bounds__(256) void calibrate_kernel(Geom g, int layer_lo, fl
   __shared__ double red[2][256];
   const LayerPtrs L = layer_ptrs(g, layer_lo + (int)blockIdx.y);
   const int h = (int)blockIdx.x, H = g.n_heads, D = g.head_dim, N = g.n_slots, NP = g.n_pad;
-  const int head = L.state[0], nv = L.state[1];
+  const int head = L.state[0], nv = L.state[1], gv = L.state[3];
   int a = head - nv;
   if (a < 0) a += N;
-  auto valid = [&](int slot) {
-    int rel = slot - a;
-    if (rel < 0) rel += N;
-    return slot < N && rel < nv;
-  };
+  auto valid = [&](int slot) { return slot_valid(g, slot, a, nv, gv); };  // ring and global slots
   const int CH = D / 16;  // 16-byte chunks per key row
   double mk = 0.0, mv = 0.0;
   for (int idx = (int)threadIdx.x; idx < NP * CH; idx += 256) {  // keys: slot-major rows
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void calibrate_kernel(Geom g, int layer_lo, fl
     }
   }
   __syncthreads();  // every thread's scale reads above are done before the scales change
-  for (int slot = (int)threadIdx.x; slot < N; slot += 256) {
+  for (int slot = (int)threadIdx.x; slot < NP; slot += 256) {
     if (!valid(slot)) continue;
     if (sk > 0.f) L.scale_k[(size_t)h * NP + slot] = sk;
     if (sv > 0.f) L.scale_v[(size_t)h * NP + slot] = sv;
@@ -223,20 +223,36 @@ hipError_t launch_calibrate(const Geom& g, int layer_lo, int layer_hi, float mar
 
 // ---------------------------------------------------------------------------
 // Fused write (the body is in write_body.h).
-template <int D, int HG>
+template <int D, int HG, bool GL = false>
 __global__ __launch_bounds__(16 * (D / 8)) void write_rope_fp8_kernel(
     Geom g, int layer, const uint4* __restrict__ k, const uint4* __restrict__ v,
-    const int32_t* __restrict__ pos, int n, const uint16_t* wk, float eps) {
-  write_rope_fp8_body<D, HG>(g, layer, k, v, pos, n, wk, eps, (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x,
-                             (int)gridDim.y);
+    const int32_t* __restrict__ pos, int n, const uint16_t* wk, float eps, int gfirst) {
+  write_rope_fp8_body<D, HG, GL>(g, layer, k, v, pos, n, wk, eps, (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x,
+                                 (int)gridDim.y, gfirst);
 }
 
-template <int D, int HG>
+template <int D, int HG, bool GL = false>
 static void launch_write_t(const Geom& g, int layer, const void* k, const void* v, const int32_t* pos,
-                           int n, const uint16_t* wk, float eps, int groups, hipStream_t s) {
+                           int n, const uint16_t* wk, float eps, int groups, hipStream_t s, int gfirst = 0) {
   dim3 grid(groups, g.n_heads / HG);
-  hipLaunchKernelGGL((write_rope_fp8_kernel<D, HG>), grid, dim3(16 * (D / 8)), 0, s, g, layer,
-                     (const uint4*)k, (const uint4*)v, pos, n, wk, eps);
+  hipLaunchKernelGGL((write_rope_fp8_kernel<D, HG, GL>), grid, dim3(16 * (D / 8)), 0, s, g, layer,
+                     (const uint4*)k, (const uint4*)v, pos, n, wk, eps, gfirst);
+}
+
+hipError_t launch_write_global(const Geom& g, int layer, int first, const void* k, const void* v, const int32_t* pos,
+                               int n, const uint16_t* wk, float eps, hipStream_t s) {
+  // 16-slot groups met by the n slots from g0 + first
+  const int b0 = g.n_ring_pad + first;
+  const int groups = (b0 + n + 15) / 16 - b0 / 16;
+  const int hg = g.n_heads % 2 == 0 ? 2 : 1;
+  if (g.head_dim == 128) {
+    if (hg == 2) launch_write_t<128, 2, true>(g, layer, k, v, pos, n, wk, eps, groups, s, first);
+    else launch_write_t<128, 1, true>(g, layer, k, v, pos, n, wk, eps, groups, s, first);
+  } else {
+    if (hg == 2) launch_write_t<64, 2, true>(g, layer, k, v, pos, n, wk, eps, groups, s, first);
+    else launch_write_t<64, 1, true>(g, layer, k, v, pos, n, wk, eps, groups, s, first);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_write(const Geom& g, int layer, const void* k, const void* v, const int32_t* pos,
@@ -299,9 +315,9 @@ __global__ __launch_bounds__(256) void rotate_kernel(Geom g, int layer_lo, int32
   bool valid[kRPT];
 #pragma unroll
   for (int k = 0; k < kRPT; ++k) {
-    const int row = (blockIdx.x * kRPT + k) * RPW + threadIdx.x / LPR;
-    const int h = row / NP;
-    slot[k] = row % NP;
+    const int row = (blockIdx.x * kRPT + k) * RPW + threadIdx.x / LPR;  // ring rows only: globals never move
+    const int h = row / g.n_ring_pad;
+    slot[k] = row % g.n_ring_pad;
     int rel = slot[k] - a;
     if (rel < 0) rel += N;
     valid[k] = h < g.n_heads && slot[k] < N && rel < nv;
@@ -362,7 +378,7 @@ hipError_t launch_rotate(const Geom& g, int layer_lo, int layer_hi, int32_t delt
   }
   const int lpr = g.head_dim / 16;
   const long long rows_per_wg = (long long)(256 / lpr) * kRPT;
-  const long long rows = (long long)g.n_heads * g.n_pad;
+  const long long rows = (long long)g.n_heads * g.n_ring_pad;
   dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg), layer_hi - layer_lo);
   if (g.head_dim == 128)
     hipLaunchKernelGGL(rotate_kernel<128>, grid, dim3(256), 0, s, g, layer_lo, delta, tab);

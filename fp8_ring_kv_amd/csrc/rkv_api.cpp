@@ -73,6 +73,12 @@ bool params_ok(const rkv_params* p, std::string* why) {
     return *why = "attn_workgroups out of range [0, 4096]", false;
   if (p->attn_merge_wait_us < -1 || p->attn_merge_wait_us > 10000)
     return *why = "attn_merge_wait_us out of range [-1, 10000]", false;
+  if (p->n_global < 0 || p->n_global > (1 << 20)) return *why = "n_global out of range [0, 2^20]", false;
+  const int32_t* b = p->rope_bands;
+  if (b[0] || b[1] || b[2]) {
+    if (b[0] < 0 || b[1] < 0 || b[2] < 0 || b[0] + b[1] + b[2] != p->head_dim / 2)
+      return *why = "rope_bands must be non-negative pair counts summing to head_dim / 2 (or all 0)", false;
+  }
   return true;
 }
 
@@ -80,11 +86,25 @@ Plan make_plan(const rkv_params* p) {
   Plan pl{};
   rkv::Geom& g = pl.g;
   const size_t H = p->n_heads, D = p->head_dim;
-  const size_t NP = align_up((size_t)p->n_slots, rkv::kTile);
+  // the ring, padded to whole tiles, then the global (sink) slots
+  const size_t NR = align_up((size_t)p->n_slots, rkv::kTile);
+  const size_t NP = NR + align_up((size_t)p->n_global, rkv::kTile);
   g.n_layers = p->n_layers;
   g.n_slots = p->n_slots;
   g.n_pad = (int32_t)NP;
   g.n_tiles = (int32_t)(NP / rkv::kTile);
+  g.n_ring_pad = (int32_t)NR;
+  g.n_ring_tiles = (int32_t)(NR / rkv::kTile);
+  g.n_global = p->n_global;
+  const int32_t* bands = p->rope_bands;
+  if (bands[0] || bands[1] || bands[2]) {
+    g.band_t = bands[0];
+    g.band_ty = bands[0] + bands[1];
+    g.pos_stride = 3;
+  } else {
+    g.band_t = g.band_ty = p->head_dim / 2;
+    g.pos_stride = 1;
+  }
   g.n_heads = p->n_heads;
   g.head_dim = p->head_dim;
   g.margin = p->scale_margin;
@@ -101,6 +121,8 @@ Plan make_plan(const rkv_params* p) {
   o = align_up(o + H * NP * 4, kAlign);
   g.off_slot_pos = o;
   o = align_up(o + NP * 4, kAlign);
+  g.off_slot_yx = o;
+  o = align_up(o + 2 * NP * 4, kAlign);
   g.off_state = o;
   o = align_up(o + rkv::kStateRegionInts * 4, kAlign);
   g.off_vmax = o;
@@ -206,9 +228,21 @@ int ring_cache_create(const rkv_params* p, void* dev_buf, size_t bytes, hipStrea
   c->ws.qexp = reinterpret_cast<int32_t*>(c->g.base + pl.ws_qexp);
   c->bytes = pl.total;
   c->norm_eps.assign(p->n_layers, -1.f);
+  // RoPE frequencies: one band of D/2 pairs, omega_j = base^(-2j/D), or three
+  // bands (t, y, x) of n_b pairs each, omega = base^(-j/n_b) within a band
   const int half = p->head_dim / 2;
   for (int j = 0; j < half; ++j) {
-    c->omega[j] = std::pow((double)p->rope_base, -2.0 * j / p->head_dim);
+    int lo = 0, nb = half;
+    if (c->g.pos_stride == 3) {
+      if (j < c->g.band_t) {
+        lo = 0, nb = c->g.band_t;
+      } else if (j < c->g.band_ty) {
+        lo = c->g.band_t, nb = c->g.band_ty - c->g.band_t;
+      } else {
+        lo = c->g.band_ty, nb = half - c->g.band_ty;
+      }
+    }
+    c->omega[j] = std::pow((double)p->rope_base, -(double)(j - lo) / nb);
     c->half_turns[j] = c->omega[j] / (2.0 * M_PI);
   }
   hipError_t e = rkv::launch_fill_zero(dev_buf, pl.total, stream);
@@ -271,6 +305,9 @@ int ring_cache_layout(const rkv_cache* c, int32_t layer, rkv_layout* out) {
   out->vmax = b + c->g.off_vmax;
   out->layer_bytes = c->g.layer_bytes;
   out->n_slots_padded = c->g.n_pad;
+  out->slot_yx = b + c->g.off_slot_yx;
+  out->n_global = c->g.n_global;
+  out->global_first_slot = c->g.n_ring_pad;
   return RKV_OK;
 }
 
@@ -291,14 +328,32 @@ int cache_write_rope_fp8(rkv_cache* c, int32_t layer, const void* k_bf16, const 
   return RKV_OK;
 }
 
+int cache_write_global(rkv_cache* c, int32_t layer, int32_t first, const void* k_bf16, const void* v_bf16,
+                       const int32_t* pos, int32_t n, hipStream_t stream) {
+  if (!c) return fail(RKV_EINVAL, "cache is null");
+  int lo, hi;
+  if (int r = layer_range(c, layer, false, &lo, &hi)) return r;
+  if (!k_bf16 || !v_bf16 || !pos) return fail(RKV_EINVAL, "null tensor pointer");
+  if (!aligned(k_bf16, 16) || !aligned(v_bf16, 16)) return fail(RKV_EINVAL, "k/v must be 16-byte aligned");
+  if (!aligned(pos, 4)) return fail(RKV_EINVAL, "pos must be 4-byte aligned");
+  if (n < 1 || first < 0 || (long long)first + n > c->p.n_global)
+    return fail(RKV_EINVAL, "global slots [" + std::to_string(first) + ", " + std::to_string((long long)first + n) +
+                                ") outside [0, n_global = " + std::to_string(c->p.n_global) + ")");
+  hipError_t e = rkv::launch_write_global(c->g, layer, first, k_bf16, v_bf16, pos, n, c->norm_k(layer),
+                                          c->norm_eps[layer], stream);
+  if (e != hipSuccess) return hip_fail(e, "global write kernel launch");
+  return RKV_OK;
+}
+
 int cache_delta_rotate(rkv_cache* c, int32_t layer, int32_t delta, hipStream_t stream) {
   if (!c) return fail(RKV_EINVAL, "cache is null");
   int lo, hi;
   if (int r = layer_range(c, layer, true, &lo, &hi)) return r;
+  // only the temporal pairs turn; spatial pairs (3-D RoPE) keep their values
   float cs[rkv::kMaxHalfDim], sn[rkv::kMaxHalfDim];
   const int half = c->p.head_dim / 2;
   for (int j = 0; j < half; ++j) {
-    const double phi = (double)delta * c->omega[j];
+    const double phi = j < c->g.band_t ? (double)delta * c->omega[j] : 0.0;
     cs[j] = (float)std::cos(phi);
     sn[j] = (float)std::sin(phi);
   }

@@ -15,7 +15,7 @@ constexpr int kMaxHalfDim = 64;  // D/2 for the largest supported head_dim (128)
 // Per-head value-scale maxima are spread over kSub slots so that no single
 // address takes more than a fraction of one launch's atomics.
 constexpr int kSub = 8;
-constexpr int kStateInts = 4;  // head, n_valid, top ticket counter of the write, 0
+constexpr int kStateInts = 4;  // head, n_valid, top ticket counter of the write, g_valid
 // A large write counts its tickets on kTicketSub sub-counters, each on its
 // own 256-byte line kTicketStride ints past the previous one (sub-counter j
 // at state[kTicketStride * (1 + j)]): atomics on one address serialize, so
@@ -27,13 +27,23 @@ constexpr int kStateRegionInts = kTicketStride * (1 + kTicketSub);
 
 // Byte offsets of one layer's arrays (relative to the layer's start) and the
 // sizes every kernel needs.  Passed by value as a kernel argument.
+// A layer's slot arrays hold the ring, slots [0, n_slots), padded to
+// n_ring_pad = a multiple of 64, then the global (sink) slots [g0, g0 +
+// n_global) with g0 = n_ring_pad, padded again: n_pad slots, n_tiles 64-slot
+// tiles, of which the first n_ring_tiles are the ring's.
 struct Geom {
   uint8_t* base;        // cache buffer
   size_t consts;        // offset of the constants block (double omega/(2 pi) table)
   size_t layer0;        // offset of layer 0
   size_t layer_bytes;   // stride between layers
-  size_t off_codes_k, off_codes_v, off_scale_k, off_scale_v, off_slot_pos, off_state, off_vmax, off_normw, off_static;
+  size_t off_codes_k, off_codes_v, off_scale_k, off_scale_v, off_slot_pos, off_slot_yx, off_state, off_vmax,
+      off_normw, off_static;
   int32_t n_layers, n_slots, n_pad, n_tiles, n_heads, head_dim;
+  int32_t n_ring_pad, n_ring_tiles, n_global;  // g0 = n_ring_pad
+  // RoPE pair bands: pairs [0, band_t) turn with the temporal position,
+  // [band_t, band_ty) with y, [band_ty, D/2) with x; pos_stride 1 (1-D
+  // positions, band_t = D/2) or 3 ((t, y, x) per token)
+  int32_t band_t, band_ty, pos_stride;
   float margin;
 };
 
@@ -43,7 +53,8 @@ struct LayerPtrs {
   float* scale_k;
   float* scale_v;
   int32_t* slot_pos;
-  int32_t* state;  // {head, n_valid, top ticket counter, 0}, sub-counters at kTicketStride * (1 + j)
+  int32_t* slot_yx;  // [2][n_pad] spatial coordinates (y, then x) of each slot (3-D RoPE)
+  int32_t* state;  // {head, n_valid, top ticket counter, g_valid}, sub-counters at kTicketStride * (1 + j)
   uint32_t* vmax;  // [H][kSub] largest value scale written since the reset (fp32
                    // bits); the head's bound is the max over its kSub entries
   uint16_t* normw; // bf16 [2][D]: RMS-norm weights of the queries, then of the keys
@@ -59,6 +70,7 @@ __host__ __device__ inline LayerPtrs layer_ptrs(const Geom& g, int layer) {
   p.scale_k = reinterpret_cast<float*>(b + g.off_scale_k);
   p.scale_v = reinterpret_cast<float*>(b + g.off_scale_v);
   p.slot_pos = reinterpret_cast<int32_t*>(b + g.off_slot_pos);
+  p.slot_yx = reinterpret_cast<int32_t*>(b + g.off_slot_yx);
   p.state = reinterpret_cast<int32_t*>(b + g.off_state);
   p.vmax = reinterpret_cast<uint32_t*>(b + g.off_vmax);
   p.normw = reinterpret_cast<uint16_t*>(b + g.off_normw);
@@ -72,6 +84,23 @@ __host__ __device__ inline LayerPtrs layer_ptrs(const Geom& g, int layer) {
 // amax 0 keeps the per-(token, head) rule).
 __device__ inline bool static_head(const LayerPtrs& L, int n_heads, int h) {
   return reinterpret_cast<const int*>(L.stat)[2 * n_heads] != 0 && L.stat[h] > 0.f && L.stat[n_heads + h] > 0.f;
+}
+
+// Whether a slot is read by the attention: a ring slot of the valid cyclic
+// range [head - n_valid, head), or a global slot below g_valid.  a = the
+// oldest valid ring slot, (head - n_valid) mod N.
+__device__ inline bool slot_valid(const Geom& g, int slot, int a, int nv, int gv) {
+  if (slot >= g.n_ring_pad) return slot - g.n_ring_pad < gv;
+  int rel = slot - a;
+  if (rel < 0) rel += g.n_slots;
+  return slot < g.n_slots && rel < nv;
+}
+
+// The position coordinate that turns RoPE pair j: t, y or x of a token whose
+// positions start at p (pos_stride ints per token).
+__device__ inline int32_t pair_coord(const Geom& g, const int32_t* p, int j) {
+  if (g.pos_stride == 1) return p[0];
+  return p[j < g.band_t ? 0 : (j < g.band_ty ? 1 : 2)];
 }
 
 __device__ inline const double* omega_turns(const Geom& g) {

@@ -36,6 +36,9 @@ hipError_t launch_calibrate(const Geom& g, int layer_lo, int layer_hi, float mar
 // pre-attention norm, null when it is off; eps its epsilon.
 hipError_t launch_write(const Geom& g, int layer, const void* k, const void* v, const int32_t* pos,
                         int n, const uint16_t* wk, float eps, hipStream_t s);
+// Global (sink) slots first .. first + n - 1 of the layer, written like the ring.
+hipError_t launch_write_global(const Geom& g, int layer, int first, const void* k, const void* v, const int32_t* pos,
+                               int n, const uint16_t* wk, float eps, hipStream_t s);
 hipError_t launch_rotate(const Geom& g, int layer_lo, int layer_hi, int32_t delta,
                          const float* cosv, const float* sinv, hipStream_t s);
 hipError_t launch_attend(const Geom& g, const AttnWs& ws, int layer, const void* q,

@@ -27,33 +27,48 @@ namespace rkv {
 // arguments, so that a launch can also run it on part of its workgroups.
 // wk: the layer's key RMS-norm weights (bf16 [D], shared by the heads) when
 // the fused pre-attention norm is on, else null; eps its epsilon.
-template <int D, int HG>
+// GL: the tokens go to the global (sink) slots gfirst .. gfirst + n - 1 (the
+// array slots g0 + gfirst + i, no wrap, no ticket); g_valid is raised to
+// gfirst + n.  The ring write (GL false) ignores gfirst.
+template <int D, int HG, bool GL = false>
 __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4* __restrict__ k,
                                            const uint4* __restrict__ v, const int32_t* __restrict__ pos,
                                            int n, const uint16_t* __restrict__ wk, float eps, int bx, int by,
-                                           int gx, int gy) {
+                                           int gx, int gy, int gfirst = 0) {
   constexpr int LPR = D / 8;  // lanes per token row
   __shared__ uint2 vcodes[HG][16][LPR];
   __shared__ float vmx[HG][16];
 
   const LayerPtrs L = layer_ptrs(g, layer);
   const int N = g.n_slots, NP = g.n_pad, H = g.n_heads;
-  const int head = L.state[0];
-  const int nvalid = L.state[1];
+  const int head = GL ? 0 : L.state[0];
+  const int nvalid = GL ? 0 : L.state[1];
   // the pages' static per-(layer, head) scales, once calibrated
   const bool smode = reinterpret_cast<const int*>(L.stat)[2 * H] != 0;
   const int h0 = by * HG;
   const int NG = (N + 15) / 16;  // 16-slot groups of the ring (the last may be short)
-  const int G = (head / 16 + bx) % NG;
+  const int b0 = g.n_ring_pad + gfirst;  // first array slot of a global write
+  const int G = GL ? b0 / 16 + bx : (head / 16 + bx) % NG;
   const int tau = threadIdx.x / LPR;
   const int lane = threadIdx.x % LPR;
+  // token written to array slot sl, or -1 (ring: (sl - head) mod N)
+  auto token_of = [&](int sl) {
+    if constexpr (GL) {
+      const int t = sl - b0;
+      return t >= 0 && t < n ? t : -1;
+    } else {
+      int t = sl - head;
+      if (t < 0) t += N;
+      return sl < N && t < n ? t : -1;
+    }
+  };
   const int slot = 16 * G + tau;
-  int i = slot - head;
-  if (i < 0) i += N;
-  const bool active = slot < N && i < n;
+  const int i = token_of(slot);
+  const bool active = i >= 0;
 
   uint4 kw[HG], vw[HG];
-  int32_t p = 0;
+  int32_t pc[4] = {0, 0, 0, 0};  // the coordinate that turns each of this lane's 4 pairs
+  int32_t pt = 0, py = 0, px = 0;
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh) kw[hh] = vw[hh] = make_uint4(0u, 0u, 0u, 0u);
   if (active) {
@@ -63,7 +78,14 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
       kw[hh] = k[row + hh * LPR];
       vw[hh] = v[row + hh * LPR];
     }
-    p = pos[i];
+    const int32_t* pp = pos + (size_t)i * g.pos_stride;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) pc[m] = pair_coord(g, pp, 4 * lane + m);
+    pt = pp[0];
+    if (g.pos_stride == 3) {
+      py = pp[1];
+      px = pp[2];
+    }
   }
   // Ticket for the device-side write position, taken once head and n_valid
   // are read (the increment depends on the loaded head; it is always 1).
@@ -92,20 +114,20 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
   for (int hh = 0; hh < HG; ++hh)
     asm volatile("" ::"v"(kw[hh].x), "v"(kw[hh].y), "v"(kw[hh].z), "v"(kw[hh].w), "v"(vw[hh].x), "v"(vw[hh].y),
                  "v"(vw[hh].z), "v"(vw[hh].w));
-  asm volatile("" ::"v"(p), "v"(tw[0]), "v"(tw[1]), "v"(tw[2]), "v"(tw[3]), "v"(wkv.x), "v"(wkv.y), "v"(wkv.z),
-               "v"(wkv.w) : "memory");
+  asm volatile("" ::"v"(pc[0]), "v"(pc[1]), "v"(pc[2]), "v"(pc[3]), "v"(tw[0]), "v"(tw[1]), "v"(tw[2]), "v"(tw[3]),
+               "v"(wkv.x), "v"(wkv.y), "v"(wkv.z), "v"(wkv.w) : "memory");
   const int wgi = by * gx + bx, nwg = gx * gy;
   const bool two_level = nwg > kTicketSplitMin;
   const int sub = wgi % kTicketSub;
   int* const counter = two_level ? L.state + kTicketStride * (1 + sub) : L.state + 2;
   int ticket = -1;
-  if (threadIdx.x == 0)
+  if (!GL && threadIdx.x == 0)
     ticket = __hip_atomic_fetch_add(counter, head < 0x7FFFFFFF ? 1 : 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // angles for every lane (the table index is always in range; inactive
   // lanes rotate zeros)
   float cs[4], sn[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) rope_cs(p, tw[m], cs[m], sn[m]);
+  for (int m = 0; m < 4; ++m) rope_cs(pc[m], tw[m], cs[m], sn[m]);
 
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh) {
@@ -181,7 +203,13 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
     vcodes[hh][tau][lane] = cv;
     if (lane == 0) vmx[hh][tau] = active ? sv : 0.f;
   }
-  if (active && lane == 0 && h0 == 0) L.slot_pos[slot] = p;
+  if (active && lane == 0 && h0 == 0) {
+    L.slot_pos[slot] = pt;
+    if (g.pos_stride == 3) {
+      L.slot_yx[slot] = py;
+      L.slot_yx[NP + slot] = px;
+    }
+  }
   // LDS-only barrier: the transpose below needs the LDS writes above, not
   // the global stores (a __syncthreads fence would wait for those too)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -196,10 +224,7 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
     int nact = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int sl = 16 * G + 8 * half + e;
-      int ii = sl - head;
-      if (ii < 0) ii += N;
-      act[e] = sl < N && ii < n;
+      act[e] = token_of(16 * G + 8 * half + e) >= 0;
       nact += act[e];
     }
     const int T = (16 * G) / kTile, w0 = (16 * G) % kTile;
@@ -230,6 +255,10 @@ __device__ inline void write_rope_fp8_body(const Geom& g, int layer, const uint4
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, vmx[threadIdx.x][e]);
     if (mx > 0.f) atomicMax(&L.vmax[(h0 + threadIdx.x) * kSub + bx % kSub], __float_as_uint(mx));
+  }
+  if constexpr (GL) {  // global slots: no ring position to advance
+    if (threadIdx.x == 0 && wgi == 0) atomicMax(&L.state[3], gfirst + n);
+    return;
   }
   // Two levels: the last workgroup of a sub-group clears its sub-counter and
   // takes a top ticket.  The one that takes the last top ticket clears the

@@ -78,24 +78,45 @@ typedef struct {
                               every merge whose partials are not complete on
                               arrival to the last arrival; results do not
                               depend on this value */
+  int32_t n_global;    /* global (sink) slots per layer beside the ring
+                          (0 .. 1<<20; 0 = none): written once per session
+                          with cache_write_global, read by every attention,
+                          never rotated (§2 "The step budget": 1,246 global
+                          slots beside a six-latent window) */
+  int32_t rope_bands[3]; /* 3-D RoPE: pairs of the head's D/2 interleaved
+                          pairs turned by the temporal position t, then by
+                          y, then by x (contiguous bands; sum D/2); each band
+                          is a RoPE of its own, omega = base^(-j / n_band)
+                          for its j-th pair; positions are then int32
+                          [n][3] = (t, y, x) per token and a reset turns
+                          only the temporal band (§4.2, Appendix G).  All 0:
+                          1-D RoPE over all pairs, omega_j = base^(-2j/D),
+                          positions int32 [n]. */
 } rkv_params;
 
 /* Byte offsets into the cache buffer for one layer.  Layout (N_pad = N
- * rounded up to 64; pad slots are zero and never valid):
+ * rounded up to 64, plus n_global rounded up to 64: the ring's slots
+ * [0, N), then the global slots [global_first_slot, + n_global) with
+ * global_first_slot = N rounded up to 64; pad slots are zero and never
+ * valid):
  *   codes_k  u8  [H][N_pad][D]        e4m3fn key codes, slot-major rows
  *   codes_v  u8  [H][N_pad/64][D][64] e4m3fn value codes, transposed per
  *                                      64-slot tile (byte w of row d = slot
  *                                      64*tile + w)
  *   scale_k  f32 [H][N_pad]           per-(slot, head) key scale
  *   scale_v  f32 [H][N_pad]           per-(slot, head) value scale
- *   slot_pos i32 [N_pad]              position each slot was written with
- *   state    i32 [576]                {head, n_valid, ...}: the next write
- *                                      slot and the number of valid slots
- *                                      (the cyclic range [head-n_valid,
- *                                      head)); the rest are ticket counters
- *                                      internal to the write kernel (a top
- *                                      counter at [2], 8 sub-counters at
- *                                      [64 (1 + j)]), zero between calls.
+ *   slot_pos i32 [N_pad]              position (3-D RoPE: temporal
+ *                                      position t) each slot was written with
+ *   slot_yx  i32 [2][N_pad]           3-D RoPE: spatial coordinates y, then x
+ *   state    i32 [576]                {head, n_valid, ., g_valid}: the next
+ *                                      write slot, the number of valid ring
+ *                                      slots (the cyclic range [head-n_valid,
+ *                                      head)) and of global slots read (1 +
+ *                                      the highest global index written);
+ *                                      the rest are ticket counters internal
+ *                                      to the write kernel (a top counter at
+ *                                      [2], 8 sub-counters at [64 (1 + j)]),
+ *                                      zero between calls.
  *   normw    bf16 [2][D]              RMS-norm weights of the queries, then
  *                                      of the keys (ring_cache_set_qk_norm)
  *   static   f32 [2][H], i32          static scales of the keys, then of the
@@ -109,6 +130,8 @@ typedef struct {
   size_t codes_k, codes_v, scale_k, scale_v, slot_pos, state, vmax;
   size_t layer_bytes; /* distance between consecutive layers */
   int32_t n_slots_padded;
+  size_t slot_yx;
+  int32_t n_global, global_first_slot;
 } rkv_layout;
 
 typedef struct rkv_cache rkv_cache; /* opaque host-side handle */
@@ -143,7 +166,8 @@ int ring_cache_layout(const rkv_cache* c, int32_t layer, rkv_layout* out);
 
 /* Ring write with RoPE and FP8 quantization fused (§4.1, §4.2, §4.3, §4.4).
  * k_bf16, v_bf16: [n][H][D] bf16 device tensors of the n new tokens.
- * pos: [n] int32 device positions.  Token i goes to slot
+ * pos: [n] int32 device positions ([n][3] = (t, y, x) with 3-D RoPE, each
+ * pair turned by its band's coordinate).  Token i goes to slot
  * (head + i) mod N; its key is rotated at pos[i] (interleaved pairs
  * (2j, 2j+1), angle pos[i] * base^(-2j/D) computed in double precision),
  * then key and value rows are quantized per (token, head):
@@ -154,16 +178,30 @@ int ring_cache_layout(const rkv_cache* c, int32_t layer, rkv_layout* out);
 int cache_write_rope_fp8(rkv_cache* c, int32_t layer, const void* k_bf16, const void* v_bf16,
                          const int32_t* pos, int32_t n, hipStream_t stream);
 
+/* Global (sink) slot write (§2 "The step budget": global slots written once
+ * per session, read by every attention, never rotated): tokens i = 0 .. n-1
+ * go to global slots first + i, with the ring write's RoPE, quantization
+ * (and static scales, RMS norm) and the same tensor layouts; the slots keep
+ * their positions.  Afterwards g_valid = max(g_valid, first + n): every
+ * global slot below g_valid is read by the attention, so the caller writes
+ * them all (ring_cache_reset sets g_valid to 0).  Requires n >= 1 and
+ * 0 <= first, first + n <= n_global. */
+int cache_write_global(rkv_cache* c, int32_t layer, int32_t first, const void* k_bf16, const void* v_bf16,
+                       const int32_t* pos, int32_t n, hipStream_t stream);
+
 /* Delta rotation at a position reset (§4.2, Appendix G): for every valid
- * slot of `layer` (all layers when layer == -1) and every head, dequantize
- * the key, rotate pair j by delta * base^(-2j/D) in fp32 (cos and sin taken
- * in double precision), take a new scale from the rotated key's amax and
- * requantize in place; slot_pos += delta.  Values are not touched. */
+ * ring slot of `layer` (all layers when layer == -1) and every head,
+ * dequantize the key, rotate pair j by delta * omega_j in fp32 (cos and sin
+ * taken in double precision; with 3-D RoPE only the temporal pairs turn,
+ * the spatial ones keep their values), take a new scale from the rotated
+ * key's amax and requantize in place; slot_pos += delta.  Values and global
+ * slots are not touched. */
 int cache_delta_rotate(rkv_cache* c, int32_t layer, int32_t delta, hipStream_t stream);
 
-/* Attention of n_q new queries over every valid slot of `layer` (§2,
- * §4.3, Appendix G).  q_bf16: [n_q][H][D] bf16 device tensor; q_pos: [n_q]
- * int32 device positions (RoPE is applied to Q here, at q_pos).  out_bf16:
+/* Attention of n_q new queries over every valid slot of `layer`, the ring's
+ * and the global slots below g_valid (§2, §4.3, Appendix G).  q_bf16:
+ * [n_q][H][D] bf16 device tensor; q_pos: [n_q] (3-D RoPE: [n_q][3]) int32
+ * device positions (RoPE is applied to Q here, at q_pos).  out_bf16:
  * [n_q][H][D] bf16 device tensor receiving softmax(q k^T / sqrt(D)) v over
  * the dequantized cache, computed with FP8 matrix instructions in the
  * configured precision, rounded to nearest even.  Non-causal.  An empty

@@ -29,7 +29,8 @@ def pos_dev(p: np.ndarray) -> torch.Tensor:
 
 
 def readback(cache: rkv.RingCache, layer: int):
-    """Host copies of (head, n_valid), slot_pos, codes_k, codes_v, scale_k, scale_v."""
+    """Host copies of (head, n_valid), slot_pos, codes_k, codes_v, scale_k, scale_v
+    (slot axes in canonical order: the ring's slots, then the global slots)."""
     torch.cuda.synchronize()
     st = cache.state(layer).cpu().numpy()
     sp = cache.slot_pos(layer).cpu().numpy().astype(np.int64)
@@ -73,10 +74,14 @@ def state_from_device(cache: rkv.RingCache, layer: int):
     holds."""
     from oracle import ring as oring
     (head, nv), sp, ck, cv, sk, sv = readback(cache, layer)
+    three_d = cache.pos_width == 3
     st = oring.RingState(cache.n_slots, cache.n_heads, cache.head_dim, rope_base=cache.params.rope_base,
                          margin=cache.params.scale_margin, head=head, n_valid=nv,
                          slot_pos=sp.copy(), codes_k=ck.copy(), codes_v=cv.copy(), scale_k=sk.copy(),
-                         scale_v=sv.copy(), vmax=cache.vmax(layer).cpu().numpy().astype(np.float64))
+                         scale_v=sv.copy(), vmax=cache.vmax(layer).cpu().numpy().astype(np.float64),
+                         n_global=cache.n_global, g_valid=int(cache.state(layer)[3].item()),
+                         bands=cache.rope_bands if three_d else None,
+                         slot_yx=cache.slot_yx(layer).cpu().numpy().astype(np.int64) if three_d else None)
     if cache.static_flag(layer):
         stat = cache.static_scales(layer).cpu().numpy().astype(np.float64)
         st.static_k, st.static_v = stat[0].copy(), stat[1].copy()
@@ -124,14 +129,18 @@ def assert_cache_matches(cache, layer, st, slots=None, check_v=True, pre=None):
     from oracle import ring as oring
     (head, nv), sp, ck, cv, sk, sv = readback(cache, layer)
     assert (head, nv) == (st.head, st.n_valid), ((head, nv), (st.head, st.n_valid))
+    assert int(cache.state(layer)[3].item()) == st.g_valid, (int(cache.state(layer)[3].item()), st.g_valid)
     # the write kernel's internal counters are back at zero after every call
     counters = cache.write_counters(layer).cpu().numpy()
-    assert len(counters) == 10 and not counters.any(), counters
+    assert len(counters) == 9 and not counters.any(), counters
     # the per-head value-scale bound equals the oracle's (fp32 values)
     vmax = cache.vmax(layer).cpu().numpy().astype(np.float64)
     assert np.array_equal(vmax, st.vmax), (vmax, st.vmax)
     valid = oring.valid_slots(st) if slots is None else slots
     assert np.array_equal(sp[valid], st.slot_pos[valid])
+    if st.bands is not None:
+        yx = cache.slot_yx(layer).cpu().numpy().astype(np.int64)
+        assert np.array_equal(yx[valid], st.slot_yx[valid])
     extra = None
     if pre is not None:
         extra = pair_ulp_bound(pre.codes_k[:, valid], pre.scale_k[:, valid])

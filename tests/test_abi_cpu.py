@@ -64,9 +64,12 @@ def test_single_hip_runtime_in_process():
 def params(**kw):
     base = dict(n_layers=1, n_slots=5788, n_heads=12, head_dim=128, max_queries=757,
                 precision=rkv.RKV_PRECISE, rope_base=10000.0, scale_margin=1.0, attn_workgroups=0,
-                attn_merge_wait_us=-1)
+                attn_merge_wait_us=-1, n_global=0, rope_bands=(0, 0, 0))
     base.update(kw)
-    return rkv.rkv_params(**base)
+    bands = base.pop("rope_bands")
+    p = rkv.rkv_params(**base)
+    p.rope_bands[:] = list(bands)
+    return p
 
 
 def test_bytes_cover_the_layout():
@@ -138,3 +141,16 @@ def test_probes_reject_misuse_without_launching():
     assert L.rkv_probe_stream(fake, 0, None) == -1
     assert L.rkv_probe_stream(fake, 24, None) == -1
     assert "multiple of 16" in probe.rkv_probe_last_error()
+
+
+def test_rope_band_and_global_parameters_are_checked():
+    assert rkv.ring_cache_bytes(params(rope_bands=(22, 21, 21), n_global=1246)) > 0
+    assert rkv.ring_cache_bytes(params(rope_bands=(22, 21, 20))) == 0  # 63 pairs, not 64
+    assert "rope_bands" in rkv.rkv_last_error()
+    assert rkv.ring_cache_bytes(params(rope_bands=(70, -3, -3))) == 0
+    assert rkv.ring_cache_bytes(params(n_global=-1)) == 0
+    assert rkv.ring_cache_bytes(params(n_global=(1 << 20) + 1)) == 0
+    # the globals add whole tiles of slot arrays to every layer
+    a = rkv.ring_cache_bytes(params(n_layers=2))
+    b = rkv.ring_cache_bytes(params(n_layers=2, n_global=1246))
+    assert b - a >= 2 * 1280 * 12 * (2 * 128 + 8)

@@ -33,7 +33,9 @@ __all__ = [
     "WRITE_ROTATE",
     "PER_CHUNK",
     "STRESS",
+    "PAGES_LAYOUT",
     "Config",
+    "frame_positions",
 ]
 
 
@@ -105,6 +107,8 @@ class Config:
     outliers: OutlierSpec = field(default_factory=OutlierSpec)
     n_layers: int = 1
     rope_base: float = 10000.0
+    n_global: int = 0          # global (sink) slots beside the ring
+    bands: tuple = None        # 3-D RoPE pairs per band (t, y, x); None: 1-D positions
 
 
 # Tiny: 1 head, head_dim 64, 64 slots, chunks of 16, 6 writes, reset d=-80.
@@ -122,6 +126,14 @@ WRITE_ROTATE = Config("write_rotate_757_h12", n_heads=12, head_dim=128, n_slots=
 # Per-chunk sequence: 60 layer caches, 4 passes, reset at chunk 42; no outliers.
 PER_CHUNK = Config("per_chunk_60x4", n_heads=12, head_dim=128, n_slots=5788, chunk=757,
                    seed=3, n_layers=60)
+
+# The pages' cache layout at one GPU's head share: 1,246 global slots written
+# once per session plus a ring of six 757-token latents (4,542 slots), 5,788
+# read by every call; 3-D RoPE with the head's 64 pairs in temporal / height /
+# width bands of 22 / 21 / 21 (synthetic: the pages give no band layout);
+# 2% outlier channels x8.
+PAGES_LAYOUT = Config("pages_g1246_r4542_h12", n_heads=12, head_dim=128, n_slots=4542, chunk=757, seed=5,
+                      outliers=OutlierSpec(0.02, 8.0), n_global=1246, bands=(22, 21, 21))
 
 # Stress: 48 heads, 11,576 slots, 1% outliers x16.
 STRESS = Config("stress_h48_11576", n_heads=48, head_dim=128, n_slots=11576, chunk=757,
@@ -155,3 +167,11 @@ class Stream:
 def positions(start: int, n: int) -> np.ndarray:
     """Consecutive int32 token positions start .. start+n-1."""
     return np.arange(start, start + n, dtype=np.int32)
+
+
+def frame_positions(t: int, n: int, width: int, first: int = 0) -> np.ndarray:
+    """3-D positions [n, 3] int32 of tokens first .. first+n-1 of one frame at
+    temporal index t, laid row-major on a grid `width` tokens wide:
+    (t, i // width, i % width)."""
+    i = np.arange(first, first + n)
+    return np.stack([np.full(n, t), i // width, i % width], axis=1).astype(np.int32)
