@@ -415,6 +415,6 @@ class RingCache:
         lay = self.layout(layer)
         H, D, NP = self.n_heads, self.head_dim, lay.n_slots_padded
         ck = self._view(lay.codes_k, H * NP * D, torch.uint8).view(H, NP, D)
-        cv = self._view(lay.codes_v, H * NP * D, torch.uint8).view(H, NP // 64, D, 64)
+        cv = self._view(lay.codes_v, H * NP * D, torch.uint8).view(H, NP // 16, D, 16)
         cv = cv.permute(0, 1, 3, 2).reshape(H, NP, D)
         return self._canon(ck, lay), self._canon(cv, lay)

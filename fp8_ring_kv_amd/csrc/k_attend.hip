@@ -249,7 +249,9 @@ struct CopyOffsets {
     const int P = wave * 64 + lane, r = P / PR, lc = (P % PR) ^ ksw<D>(r);
     k = (uint32_t)((r - wave * (64 / PR)) * D + 16 * lc);
     const int d = lane >> 2;  // row within a V chunk (16 rows of 64 bytes)
-    v = (uint32_t)(64 * d + 16 * ((lane & 3) ^ vsw(d)));
+    // source: 16-slot sub-tile p = (lane & 3) ^ vsw(d) of the tile, row d of
+    // the chunk's 16 (the cache stores V^T as [16-slot group][D][16])
+    v = (uint32_t)(16 * D * ((lane & 3) ^ vsw(d)) + 16 * d);
   }
 };
 
@@ -270,7 +272,7 @@ __device__ inline void copy_tile(lds_u8* lbuf, const TileSrc& src, int T, const 
   for (int j = 0; j < KC / 4; ++j) {
     const int c = wave + 4 * j;
     copy16(kt + c * 1024 + co.k, lbuf + c * 1024);
-    copy16(vt + c * 1024 + co.v, lbuf + TileLds<D>::V_OFF + c * 1024);
+    copy16(vt + c * 256 + co.v, lbuf + TileLds<D>::V_OFF + c * 1024);
   }
   // scales: waves 0, 1 copy s_k[32 w, +32), waves 2, 3 s_v[32 (w - 2), +32),
   // 4 per lane on lanes 0..7
@@ -622,7 +624,7 @@ __global__ __launch_bounds__(256) void q_prep_kernel(QPrepArgs A) {
 }
 
 // Write and query preparation in one launch (D = 128: both use 256-thread
-// workgroups): the first wgx * wgy workgroups write the new tokens, the rest
+// workgroups): the first wgs workgroups write the new tokens, the rest
 // prepare the queries.  The two touch disjoint memory.
 struct WritePrepArgs {
   QPrepArgs P;
@@ -631,16 +633,16 @@ struct WritePrepArgs {
   const uint4* v;
   const int32_t* pos;
   int n;
-  int wgx, wgy;  // the write's grid
+  int groups, items, wgs;  // the write's work items and workgroups (write_grid)
   const uint16_t* wk;  // key RMS-norm weights, null when off (epsilon in P.eps)
 };
 
 template <int HG, int TERMS>
 __global__ __launch_bounds__(256) void write_prep_kernel(WritePrepArgs W) {
-  const int b = (int)blockIdx.x, nw = W.wgx * W.wgy;
+  const int b = (int)blockIdx.x, nw = W.wgs;
   if (b < nw)
-    write_rope_fp8_body<128, HG>(W.P.g, W.layer, W.k, W.v, W.pos, W.n, W.wk, W.P.eps, b % W.wgx, b / W.wgx, W.wgx,
-                                 W.wgy);
+    write_rope_fp8_body<128, HG>(W.P.g, W.layer, W.k, W.v, W.pos, W.n, W.wk, W.P.eps, b, nw, W.groups, W.items, b,
+                                 nw);
   else
     q_prep_body<128, q_terms<TERMS>()>(W.P, b - nw);
 }
@@ -853,13 +855,37 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
       qs[t] = A.ws.qexp[row];
     }
   };
+  // The ring state first: vector loads complete in issue order, so a state
+  // read issued after the queries' loads would wait for all of them.
+  const int head = L.state[0], nv = L.state[1], gv = L.state[3];
   // With a grid that is a multiple of the unit count, every range lies in
   // unit gi / (G / U) whatever the ring holds: its queries load while the
   // ring state is read.
   const int u_pre = G % U == 0 ? gi / (G / U) : -1;
-  if (u_pre >= 0) load_q(u_pre);
-
-  const int head = L.state[0], nv = L.state[1], gv = L.state[3];
+  // The head's value bound and static-scale mode: read for that unit here,
+  // before this kernel stores anything, they are scalar loads that no wait
+  // for the queries' vector loads holds up (read in the loop they would
+  // delay the first tile copies by the queries' round trip).
+  auto head_consts = [&](int h, uint32_t& vm, bool& sh, float& svh) {
+    vm = 0u;  // the head's bound: max over its kSub slots (bit order = value order)
+#pragma unroll
+    for (int k2 = 0; k2 < kSub; ++k2) vm = max(vm, L.vmax[h * kSub + k2]);
+    // the pages' static per-head scales (every valid slot of the head
+    // carries them): P' = 7 P with no per-slot factor, s_v on the output
+    // (static_head, with the three words read together rather than one
+    // after another)
+    const int on = reinterpret_cast<const int*>(L.stat)[2 * H];
+    const float skh = L.stat[h], svv = L.stat[H + h];
+    sh = (on != 0) & (skh > 0.f) & (svv > 0.f);
+    svh = sh ? svv : 1.f;
+  };
+  uint32_t vm_pre = 0u;
+  bool sh_pre = false;
+  float svh_pre = 1.f;
+  if (u_pre >= 0) {
+    load_q(u_pre);
+    head_consts(u_pre / A.nqg, vm_pre, sh_pre, svh_pre);
+  }
   int a = head - nv;
   if (a < 0) a += N;
   const int NTR = g.n_ring_tiles;
@@ -908,15 +934,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
     x += t_hi - t_lo;
     const int nk = t_hi - t_lo;
     const int h = u / A.nqg, qg = u % A.nqg;
-    uint32_t vm = 0u;  // the head's bound: max over its kSub slots (bit order = value order)
-#pragma unroll
-    for (int k2 = 0; k2 < kSub; ++k2) vm = max(vm, L.vmax[h * kSub + k2]);
+    uint32_t vm = vm_pre;
+    bool sh = sh_pre;
+    float svh = svh_pre;
+    if (u != u_pre) head_consts(h, vm, sh, svh);
     const float vmaxh = __uint_as_float(vm);
     const float ch = vmaxh > 0.f ? kE4M3Max / (kHeadroom * vmaxh) : 1.f;
-    // the pages' static per-head scales (every valid slot of the head
-    // carries them): P' = 7 P with no per-slot factor, s_v on the output
-    const bool sh = static_head(L, H, h);
-    const float svh = sh ? L.stat[H + h] : 1.f;
     const float l2c = sh ? kLog2Seven : __log2f(ch);
     TileSrc src;
     src.kbase = L.codes_k + (size_t)h * NP * D;
@@ -1175,9 +1198,8 @@ hipError_t launch_write_attend(const Geom& g, const AttnWs& ws, int layer, const
   W.pos = pos;
   W.n = n;
   int hg;
-  write_grid(g, n, &W.wgx, &hg);
-  W.wgy = g.n_heads / hg;
-  const int blocks = W.wgx * W.wgy + prep_blocks(W.P);
+  write_grid(g, n, &W.groups, &hg, &W.items, &W.wgs);
+  const int blocks = W.wgs + prep_blocks(W.P);
   if (hg == 2) launch_write_prep_t<2>(W, blocks, ws.terms, s);
   else launch_write_prep_t<1>(W, blocks, ws.terms, s);
   hipError_t e = hipGetLastError();

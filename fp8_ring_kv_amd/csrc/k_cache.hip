@@ -114,11 +114,10 @@ __global__ __launch_bounds__(256) void calibrate_kernel(Geom g, int layer_lo, fl
     const uint4 w = *reinterpret_cast<const uint4*>(L.codes_k + ((size_t)h * NP + slot) * D + 16 * c);
     mk = max16_scaled(w, L.scale_k + (size_t)h * NP + slot, false, mk);
   }
-  for (int idx = (int)threadIdx.x; idx < g.n_tiles * D * 4; idx += 256) {  // values: [tile][d][64 slots]
+  for (int idx = (int)threadIdx.x; idx < g.n_tiles * D * 4; idx += 256) {  // values: [16-slot group][d][16 slots]
     const int tile = idx / (D * 4), d = (idx / 4) % D, qtr = idx % 4;
     const int s0 = kTile * tile + 16 * qtr;
-    const uint4 w = *reinterpret_cast<const uint4*>(L.codes_v + (((size_t)h * g.n_tiles + tile) * D + d) * kTile +
-                                                    16 * qtr);
+    const uint4 w = *reinterpret_cast<const uint4*>(L.codes_v + (((size_t)h * 4 * g.n_tiles + 4 * tile + qtr) * D + d) * 16);
     float sc[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) sc[e] = valid(s0 + e) ? L.scale_v[(size_t)h * NP + s0 + e] : 0.f;
@@ -187,7 +186,7 @@ __global__ __launch_bounds__(256) void calibrate_kernel(Geom g, int layer_lo, fl
         sc[e] = ok ? L.scale_v[(size_t)h * NP + s0 + e] : 0.f;
       }
       if (!any) continue;
-      uint4* p = reinterpret_cast<uint4*>(L.codes_v + (((size_t)h * g.n_tiles + tile) * D + d) * kTile + 16 * qtr);
+      uint4* p = reinterpret_cast<uint4*>(L.codes_v + (((size_t)h * 4 * g.n_tiles + 4 * tile + qtr) * D + d) * 16);
       const uint4 old = *p;
       const uint4 nw = requant16(old, sc, true, sv);
       // slots outside the valid range keep their bytes
@@ -226,17 +225,17 @@ hipError_t launch_calibrate(const Geom& g, int layer_lo, int layer_hi, float mar
 template <int D, int HG, bool GL = false>
 __global__ __launch_bounds__(16 * (D / 8)) void write_rope_fp8_kernel(
     Geom g, int layer, const uint4* __restrict__ k, const uint4* __restrict__ v,
-    const int32_t* __restrict__ pos, int n, const uint16_t* wk, float eps, int gfirst) {
-  write_rope_fp8_body<D, HG, GL>(g, layer, k, v, pos, n, wk, eps, (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x,
-                                 (int)gridDim.y, gfirst);
+    const int32_t* __restrict__ pos, int n, const uint16_t* wk, float eps, int groups, int items, int gfirst) {
+  const int b = (int)blockIdx.x, nw = (int)gridDim.x;
+  write_rope_fp8_body<D, HG, GL>(g, layer, k, v, pos, n, wk, eps, b, nw, groups, items, b, nw, gfirst);
 }
 
 template <int D, int HG, bool GL = false>
 static void launch_write_t(const Geom& g, int layer, const void* k, const void* v, const int32_t* pos,
-                           int n, const uint16_t* wk, float eps, int groups, hipStream_t s, int gfirst = 0) {
-  dim3 grid(groups, g.n_heads / HG);
-  hipLaunchKernelGGL((write_rope_fp8_kernel<D, HG, GL>), grid, dim3(16 * (D / 8)), 0, s, g, layer,
-                     (const uint4*)k, (const uint4*)v, pos, n, wk, eps, gfirst);
+                           int n, const uint16_t* wk, float eps, int groups, int items, int wgs, hipStream_t s,
+                           int gfirst = 0) {
+  hipLaunchKernelGGL((write_rope_fp8_kernel<D, HG, GL>), dim3(wgs), dim3(16 * (D / 8)), 0, s, g, layer,
+                     (const uint4*)k, (const uint4*)v, pos, n, wk, eps, groups, items, gfirst);
 }
 
 hipError_t launch_write_global(const Geom& g, int layer, int first, const void* k, const void* v, const int32_t* pos,
@@ -245,26 +244,28 @@ hipError_t launch_write_global(const Geom& g, int layer, int first, const void* 
   const int b0 = g.n_ring_pad + first;
   const int groups = (b0 + n + 15) / 16 - b0 / 16;
   const int hg = g.n_heads % 2 == 0 ? 2 : 1;
+  const int items = groups * (g.n_heads / hg);
+  const int wgs = items < kWriteMaxWgs ? items : kWriteMaxWgs;
   if (g.head_dim == 128) {
-    if (hg == 2) launch_write_t<128, 2, true>(g, layer, k, v, pos, n, wk, eps, groups, s, first);
-    else launch_write_t<128, 1, true>(g, layer, k, v, pos, n, wk, eps, groups, s, first);
+    if (hg == 2) launch_write_t<128, 2, true>(g, layer, k, v, pos, n, wk, eps, groups, items, wgs, s, first);
+    else launch_write_t<128, 1, true>(g, layer, k, v, pos, n, wk, eps, groups, items, wgs, s, first);
   } else {
-    if (hg == 2) launch_write_t<64, 2, true>(g, layer, k, v, pos, n, wk, eps, groups, s, first);
-    else launch_write_t<64, 1, true>(g, layer, k, v, pos, n, wk, eps, groups, s, first);
+    if (hg == 2) launch_write_t<64, 2, true>(g, layer, k, v, pos, n, wk, eps, groups, items, wgs, s, first);
+    else launch_write_t<64, 1, true>(g, layer, k, v, pos, n, wk, eps, groups, items, wgs, s, first);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_write(const Geom& g, int layer, const void* k, const void* v, const int32_t* pos,
                         int n, const uint16_t* wk, float eps, hipStream_t s) {
-  int groups, hg;
-  write_grid(g, n, &groups, &hg);
+  int groups, hg, items, wgs;
+  write_grid(g, n, &groups, &hg, &items, &wgs);
   if (g.head_dim == 128) {
-    if (hg == 2) launch_write_t<128, 2>(g, layer, k, v, pos, n, wk, eps, groups, s);
-    else launch_write_t<128, 1>(g, layer, k, v, pos, n, wk, eps, groups, s);
+    if (hg == 2) launch_write_t<128, 2>(g, layer, k, v, pos, n, wk, eps, groups, items, wgs, s);
+    else launch_write_t<128, 1>(g, layer, k, v, pos, n, wk, eps, groups, items, wgs, s);
   } else {
-    if (hg == 2) launch_write_t<64, 2>(g, layer, k, v, pos, n, wk, eps, groups, s);
-    else launch_write_t<64, 1>(g, layer, k, v, pos, n, wk, eps, groups, s);
+    if (hg == 2) launch_write_t<64, 2>(g, layer, k, v, pos, n, wk, eps, groups, items, wgs, s);
+    else launch_write_t<64, 1>(g, layer, k, v, pos, n, wk, eps, groups, items, wgs, s);
   }
   return hipGetLastError();
 }

@@ -60,16 +60,25 @@ hipError_t launch_write_attend(const Geom& g, const AttnWs& ws, int layer, const
                                const int32_t* pos, int n, const void* q, const int32_t* q_pos, int n_q,
                                void* out, const uint16_t* wq, const uint16_t* wk, float eps, hipStream_t s);
 
-// Grid of the write: `groups` 16-slot groups (a run of n slots meets at most
-// n/16 + 2 of them) times n_heads / hg head groups of hg heads.  Two heads per
-// workgroup: the write is bound by each wave's arithmetic latency, and 4 heads
-// per workgroup ran 0.5 us slower (fewer, longer waves over the compute units).
-inline void write_grid(const Geom& g, int n, int* groups, int* hg) {
+// Work of the write: `groups` 16-slot groups (a run of n slots meets at most
+// n/16 + 2 of them) times n_heads / hg head groups of hg heads, the items.
+// Two heads per item: the write is bound by each wave's arithmetic latency,
+// and 4 heads per workgroup ran 0.5 us slower (fewer, longer waves over the
+// compute units).  *wgs workgroups take them: one item each up to
+// kWriteMaxWgs, several each beyond (a persistent grid whose workgroups load
+// their next item while they process the current one).
+#ifndef RKV_WRITE_MAX_WGS
+#define RKV_WRITE_MAX_WGS 1024
+#endif
+constexpr int kWriteMaxWgs = RKV_WRITE_MAX_WGS;
+inline void write_grid(const Geom& g, int n, int* groups, int* hg, int* items, int* wgs) {
   const int NG = (g.n_slots + 15) / 16;
   *groups = (n + 15) / 16 + 2;
   if (*groups > NG) *groups = NG;
   const int H = g.n_heads;
   *hg = H % 2 == 0 ? 2 : 1;
+  *items = *groups * (H / *hg);
+  *wgs = *items < kWriteMaxWgs ? *items : kWriteMaxWgs;
 }
 
 }  // namespace rkv

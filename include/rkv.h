@@ -100,9 +100,9 @@ typedef struct {
  * global_first_slot = N rounded up to 64; pad slots are zero and never
  * valid):
  *   codes_k  u8  [H][N_pad][D]        e4m3fn key codes, slot-major rows
- *   codes_v  u8  [H][N_pad/64][D][64] e4m3fn value codes, transposed per
- *                                      64-slot tile (byte w of row d = slot
- *                                      64*tile + w)
+ *   codes_v  u8  [H][N_pad/16][D][16] e4m3fn value codes, transposed per
+ *                                      16-slot group (byte w of row d =
+ *                                      slot 16*group + w)
  *   scale_k  f32 [H][N_pad]           per-(slot, head) key scale
  *   scale_v  f32 [H][N_pad]           per-(slot, head) value scale
  *   slot_pos i32 [N_pad]              position (3-D RoPE: temporal
