@@ -61,6 +61,10 @@ def parse():
                     help="persistent workgroups per attention call (0 = one per compute unit)")
     ap.add_argument("--no-graph", action="store_true",
                     help="report the eager launches as value (no HIP-graph capture and replay)")
+    ap.add_argument("--upkeep-only", action="store_true",
+                    help="run only a few launches of the cache-upkeep kernels at their bandwidth shapes "
+                         "(60-layer rotation, a whole-ring write, the 48-head write) and exit: "
+                         "the command that the byte counters of those kernels are taken on")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the steps, run one plain copy kernel over this many MiB "
                          "(fp32 negation, read + write): the reference for HBM byte counters")
@@ -68,6 +72,7 @@ def parse():
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attend_757x5788_h12_hbm_traffic.md")
+COUNTER_RECORD = os.path.join(ROOT, "profiles", "attend_757x5788_h12_counters.md")
 ATTEND_SOURCES = ["k_attend.hip", "rkv_device.h", "rkv_launch.h"]
 
 
@@ -80,23 +85,28 @@ def attend_source_digest():
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per attention call from the committed counter record, or None when
+def recorded_value(path, key):
+    """A per-call figure from a committed counter record (profiles/), or None when
     the record is absent or was taken on different attention sources."""
     try:
-        with open(TRAFFIC_RECORD) as f:
+        with open(path) as f:
             text = f.read()
     except OSError:
         return None
     fields = {}
     for line in text.splitlines():
         line = line.strip().strip("`")
-        if line.startswith("sources_sha256:") or line.startswith("hbm_bytes_per_call:"):
+        if line.startswith("sources_sha256:") or line.startswith(key + ":"):
             k, v = line.split(":", 1)
             fields[k] = v.strip()
-    if fields.get("sources_sha256") != attend_source_digest() or "hbm_bytes_per_call" not in fields:
+    if fields.get("sources_sha256") != attend_source_digest() or key not in fields:
         return None
-    return float(fields["hbm_bytes_per_call"])
+    return float(fields[key])
+
+
+def recorded_traffic():
+    """HBM bytes per attention call (both kernels), from the byte-counter record."""
+    return recorded_value(TRAFFIC_RECORD, "hbm_bytes_per_call")
 
 
 def to_dev(x):
@@ -216,6 +226,46 @@ def capture_steps(cache, pool, pos_pool, out, first, steps):
     return g
 
 
+def upkeep_only(args, rkv, pool, pos_pool, prec, dev):
+    """A few launches of each cache-upkeep kernel at its bandwidth shape: the
+    60-layer rotation (2 launches), a whole-ring write of 5,788 tokens x 12
+    heads (3 launches) and the 48-head 757-token write (3 launches)."""
+    import torch
+    big = rkv.RingCache(60, N, H, D, CHUNK, prec, device=dev)
+    for layer in range(60):
+        for c in range(8):
+            q, k, v = pool[(layer + c) % RESET_EVERY]
+            big.write(layer, k, v, pos_pool[c])
+    torch.cuda.synchronize()
+    for d in (1, -1):
+        big.rotate(-1, d)
+    torch.cuda.synchronize()
+    del big
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    fr = rkv.RingCache(1, N, H, D, CHUNK, prec, device=dev)
+    kf = torch.randn(N, H, D, generator=gen, device=dev).to(torch.bfloat16)
+    vf = torch.randn(N, H, D, generator=gen, device=dev).to(torch.bfloat16)
+    pf = torch.arange(N, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        fr.write(0, kf, vf, pf)
+    torch.cuda.synchronize()
+    del fr, kf, vf, pf
+    st = rkv.RingCache(1, 11576, 48, D, CHUNK, prec, device=dev)
+    ks = torch.randn(CHUNK, 48, D, generator=gen, device=dev).to(torch.bfloat16)
+    for c in range(3):
+        st.write(0, ks, ks, pos_pool[0] + CHUNK * c)
+    torch.cuda.synchronize()
+    if args.copy_mib:  # the byte counters' reference kernel, as in the full run
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    print(json.dumps({"upkeep_only": True, "rotate_60layer_launches": 2, "write_full_ring_launches": 3,
+                      "write_48head_launches": 3}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -255,6 +305,10 @@ def main():
     # positions of the 42 chunks of a reset period (after each reset the cached
     # positions move back by 42 * 757, so new chunks reuse the same ones)
     pos_pool = [pos_base + (8888 + CHUNK * j) for j in range(RESET_EVERY)]
+
+    if args.upkeep_only:
+        upkeep_only(args, rkv, pool, pos_pool, prec, dev)
+        return
 
     def step(i):
         j = i % RESET_EVERY
@@ -482,6 +536,11 @@ def main():
                            "kernel": "cache_attend call = q_prep_kernel + attend_kernel",
                            "per_launch_flop": ATTN_FLOP,
                            "per_launch_us": round(comp["attend_us"], 3)}
+        busy = recorded_value(COUNTER_RECORD, "mfma_busy_cycles_per_call")
+        if busy is not None:
+            # matrix-core busy cycles (counter record) over the SIMD-cycles of the timed call
+            simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+            res["roofline"]["mfma_busy_frac"] = round(busy / (simds * 2.4e9 * comp["attend_us"] * 1e-6), 4)
         if peaks:
             res["roofline"]["frac_of_measured_peak"] = round(achieved / peaks["fp8_mfma_TFLOPs"], 4)
     if "attend_static_us" in comp:
