@@ -13,8 +13,9 @@
 // attention proper:
 //
 // Work: unit u = (head h, group qg of 128 queries), u = h * nqg + qg; each
-// unit needs `count` 64-slot tiles (the tiles holding valid slots, in cyclic
-// order from the tile of the oldest valid slot).  A persistent grid of G
+// unit needs `count` 64-slot tiles (the ring tiles holding valid slots, in
+// cyclic order from the tile of the oldest valid slot, then the tiles of the
+// valid global slots).  A persistent grid of G
 // 4-wave workgroups, two per compute unit, cuts the unit-major list of all
 // units * count (unit, tile) pairs into G equal contiguous ranges; when the
 // units are fewer than the workgroup slots, G is a multiple of the unit
@@ -37,8 +38,10 @@
 //      come from different workgroups, so their matrix and vector phases
 //      overlap;
 //   3. a whole unit writes its bf16 output; a unit split between
-//      workgroups writes a partial (O, max, sum) per wave and the last
-//      workgroup to finish its part merges the partials.
+//      workgroups writes a partial (O, max, sum) per wave, and the unit's
+//      16 output blocks are merged by the workgroups whose ranges end in it
+//      (each its share, after a bounded wait for the unit's last tile) or by
+//      the last to arrive.
 //
 // Probability scale: c_h = 448 / (64 vmax_h), vmax_h being the largest value
 // scale written to head h since the reset (kept by the write kernel).  The
