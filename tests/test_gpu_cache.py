@@ -107,13 +107,15 @@ def test_large_writes_take_two_level_tickets():
     """A 2,000-token write at 12 heads is 762 workgroups, above the 512 that
     count their tickets on one counter: the ring position must still advance
     exactly once per call, with every counter back at zero, before and after
-    a small write that uses the single counter."""
-    cfg = Config("bigwrite", n_heads=12, head_dim=128, n_slots=2100, chunk=0, seed=12,
+    a small write that uses the single counter.  A 4,000-token write is 1,512
+    work items for 1,024 workgroups: some take two, loading the second while
+    they store the first (and it wraps the ring)."""
+    cfg = Config("bigwrite", n_heads=12, head_dim=128, n_slots=4100, chunk=0, seed=12,
                  outliers=OutlierSpec(0.02, 8.0))
     cache, st = new_pair(cfg)
     s = Stream(cfg)
     p0 = 0
-    for n in (2000, 300, 2000):
+    for n in (2000, 300, 2000, 4000):
         _, k, v = s.chunk(n)
         pos = positions(p0, n)
         cache.write(0, to_dev(k), to_dev(v), pos_dev(pos))

@@ -65,6 +65,35 @@ def test_noalloc_attention_on_a_wrapped_partial_cache_and_empty_layer():
         assert not got.float().abs().sum().item()
 
 
+def test_noalloc_attention_over_globals_and_3d_ring_with_static_heads():
+    """The paper's layout in small (global slots beside a 3-D RoPE ring), then
+    with static scales: the fixed-scratch call gives cache_attend's bits."""
+    require_gpu()
+    from workloads import frame_positions
+    bands = (22, 21, 21)
+    cfg = Config("noalloc_g3d", n_heads=4, head_dim=128, n_slots=300, chunk=100, seed=43,
+                 outliers=OutlierSpec(0.02, 8.0), n_global=90, bands=bands)
+    cache = rkv.RingCache(1, 300, 4, 128, 100, device=DEV, n_global=90, rope_bands=bands)
+    p3 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+    s = Stream(cfg)
+    _, k, v = s.chunk(90)
+    cache.write_global(0, 0, to_dev(k), to_dev(v), p3(frame_positions(-1, 90, 10)))
+    for t in range(4):  # 400 tokens into 300 ring slots: wraps
+        _, k, v = s.chunk()
+        cache.write(0, to_dev(k), to_dev(v), p3(frame_positions(t, 100, 10)))
+    for static in (False, True):
+        if static:
+            cache.calibrate_static(0, 1.5)
+        for n_q in (100, 33):
+            q, _, _ = s.chunk(n_q)
+            qd, qpos = to_dev(q), p3(frame_positions(3, n_q, 10))
+            want = cache.attend(0, qd, qpos)
+            got = torch.full_like(want, float("nan"))
+            _attend_noalloc(cache, 0, qd, qpos, got)
+            torch.cuda.synchronize()
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), (static, n_q)
+
+
 def test_noalloc_rejects_a_workspace_beyond_the_fixed_scratch():
     require_gpu()
     # 96 heads x 1,024 queries: (768 + 512) units+workgroups x 34 KiB > 32 MiB
