@@ -610,7 +610,12 @@ __device__ inline void q_prep_body(const QPrepArgs& A, int block) {
       }
     }
     const size_t row = ((size_t)t * H + h) * A.ws.nq_pad + qi;
-    uint8_t* dst = A.ws.qcodes + row * D + part * EPT;
+    // codes in the order the attention's lanes read them as matrix operands
+    // (qcodes in rkv_launch.h): dims [d0, d0 + EPT) lie in 32-byte chunk
+    // d0 / 32 of the row, block ks = d0 / 64, lane half gq = chunk % 2
+    const int d0 = part * EPT;
+    const size_t opnd = ((row / 32) * (D / 64) + d0 / 64) * 64 + (qi % 32) + 32 * ((d0 / 32) % 2);
+    uint8_t* dst = A.ws.qcodes + opnd * 32 + d0 % 32;
     if constexpr (EPT == 16) {
       *reinterpret_cast<uint4*>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
     } else {
@@ -853,8 +858,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const size_t row = ((size_t)t * H + h) * A.ws.nq_pad + qi;
+      // lane l's 32 bytes of block ks are at operand index ((32-row block) KS + ks) 64 + l:
+      // each wave's loads are contiguous 2 KiB
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[t][ks] = gload32(A.ws.qcodes + row * D + 64 * ks + 32 * gq);
+      for (int ks = 0; ks < KS; ++ks) qf[t][ks] = gload32(A.ws.qcodes + (((row / 32) * KS + ks) * 64 + lane) * 32);
       qs[t] = A.ws.qexp[row];
     }
   };

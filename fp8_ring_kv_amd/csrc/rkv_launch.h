@@ -19,7 +19,11 @@ struct AttnWs {
   // line: tiles arrived (low half) | output blocks committed to a merge
   // (high half); zeroed for the call's units by q_prep_kernel
   unsigned long long* sync;
-  uint8_t* qcodes; // [3 terms][H][nq_pad][D] e4m3 codes of the RoPE'd queries
+  // e4m3 codes of the RoPE'd queries, 3 terms x H x nq_pad rows x D, in
+  // matrix-operand order: per term, head and block of 32 rows, per k-block
+  // ks of 64 dims, 64 lanes x 32 bytes -- lane li + 32 gq holds dims
+  // [64 ks + 32 gq, +32) of the block's row li
+  uint8_t* qcodes;
   int32_t* qexp;   // [3 terms][H][nq_pad] E8M0 code (127 + e) of the 2^e scale of each query row and term
   int32_t nq_pad;  // max_queries rounded up to 128
   int32_t grid;    // persistent workgroups
