@@ -66,11 +66,15 @@ hipError_t launch_write_attend(const Geom& g, const AttnWs& ws, int layer, const
 
 // Work of the write: `groups` 16-slot groups (a run of n slots meets at most
 // n/16 + 2 of them) times n_heads / hg head groups of hg heads, the items.
-// Two heads per item: the write is bound by each wave's arithmetic latency,
-// and 4 heads per workgroup ran 0.5 us slower (fewer, longer waves over the
-// compute units).  *wgs workgroups take them: one item each up to
-// kWriteMaxWgs, several each beyond (a persistent grid whose workgroups load
-// their next item while they process the current one).
+// A write is bound by each wave's arithmetic latency: one head per item while
+// the items fit in one resident grid (the 757-token, 12-head write: 612
+// workgroups; beside the query preparation its chain ended 1.5 us sooner
+// than with two heads), two heads per item for larger writes (one head per
+// item slowed them by 30-50%: twice the items over a grid that is already
+// full; four heads per workgroup ran 0.5 us slower still).  *wgs workgroups
+// take them: one item each up to kWriteMaxWgs, several each beyond (a
+// persistent grid whose workgroups load their next item while they process
+// the current one).
 #ifndef RKV_WRITE_MAX_WGS
 #define RKV_WRITE_MAX_WGS 1024
 #endif
@@ -80,7 +84,7 @@ inline void write_grid(const Geom& g, int n, int* groups, int* hg, int* items, i
   *groups = (n + 15) / 16 + 2;
   if (*groups > NG) *groups = NG;
   const int H = g.n_heads;
-  *hg = H % 2 == 0 ? 2 : 1;
+  *hg = H % 2 == 0 && *groups * H > kWriteMaxWgs ? 2 : 1;
   *items = *groups * (H / *hg);
   *wgs = *items < kWriteMaxWgs ? *items : kWriteMaxWgs;
 }
