@@ -124,6 +124,26 @@ def test_large_writes_take_two_level_tickets():
         assert_cache_matches(cache, 0, st)
 
 
+def test_writes_across_the_heads_per_item_switch():
+    """A write takes one head per work item while its items (16-slot groups
+    met, n/16 + 2, times heads) fit 1,024 workgroups, two heads per item
+    beyond: at 12 heads 1,328 tokens are 85 x 12 = 1,020 one-head items and
+    1,344 tokens 86 x 6 = 516 two-head items.  Both sides, at ring offsets
+    that leave partial groups at each end and wrap, bit-checked."""
+    cfg = Config("hgswitch", n_heads=12, head_dim=128, n_slots=3000, chunk=0, seed=21,
+                 outliers=OutlierSpec(0.02, 8.0))
+    cache, st = new_pair(cfg)
+    s = Stream(cfg)
+    p0 = 0
+    for n in (7, 1328, 1344, 1344, 1328):
+        _, k, v = s.chunk(n)
+        pos = positions(p0, n)
+        cache.write(0, to_dev(k), to_dev(v), pos_dev(pos))
+        oring.write(st, k.f64, v.f64, pos)
+        p0 += n
+        assert_cache_matches(cache, 0, st)
+
+
 @pytest.mark.parametrize("head_dim", [64, 128])
 def test_wrapping_writes_of_varied_sizes(head_dim):
     """Random write sizes (1 .. N, including a full-ring write) wrap the ring many times."""
