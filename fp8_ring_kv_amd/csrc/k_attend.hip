@@ -727,32 +727,40 @@ __device__ inline void store_ml(const PartRsrc& pr, int idx, float m, float l) {
 
 // Merge of one output block of split unit u: query slice qs (32 queries) x
 // dim block b (32 dims), over all the unit's segments in segment order, by
-// one wave (the same arithmetic whichever wave and workgroup does it).  The
-// segment of the workgroup range holding (unit, tile) pair y is
-// floor(((y + 1) G - 1) / W); the next starts at that range's end.
-// Segments are taken kMB at a time, their loads issued together; a short
-// batch points its spare loads past the end of the buffer, which returns
-// zeros without a memory access.
+// one wave (the same arithmetic whichever wave and workgroup does it).  With
+// an even split (ek > 0 ranges per unit, none empty) the unit's ranges are
+// u ek .. u ek + ek - 1.  Otherwise the segment of the workgroup range
+// holding (unit, tile) pair y is floor(((y + 1) G - 1) / W), and the next
+// starts at that range's end.  Segments are taken kMB at a time, their loads
+// issued together; a short batch points its spare loads past the end of the
+// buffer, which returns zeros without a memory access.
 template <int D>
 __device__ __attribute__((always_inline)) inline void merge_block(const PartRsrc& pr, int u, int count, long long W,
-                                                                  int G, int qs, int b, int lane, uint16_t* orow,
-                                                                  bool store, float ch, int gq) {
+                                                                  int G, int ek, int qs, int b, int lane,
+                                                                  uint16_t* orow, bool store, float ch, int gq) {
   constexpr int CH = D / 16, kMB = 8;
   constexpr int kPast = 0x40000000;  // a byte offset beyond any partial buffer
   const long long uhi = (long long)(u + 1) * count;
   long long y = (long long)u * count;
+  int j0 = 0;  // even split: the batch's first range of the unit
   float Mu = -INFINITY, Lu = 0.f;
   v16f acc = v16f{};
-  while (y < uhi) {
+  while (ek > 0 ? j0 < ek : y < uhi) {
     int sg[kMB];
     bool ok[kMB];
 #pragma unroll
     for (int k = 0; k < kMB; ++k) {
-      const long long w = y < uhi ? ((y + 1) * G - 1) / W : -1;
-      ok[k] = w >= 0;
-      sg[k] = (int)w + u;
-      if (ok[k]) y = (w + 1) * W / G;
+      if (ek > 0) {
+        ok[k] = j0 + k < ek;
+        sg[k] = u * ek + j0 + k + u;
+      } else {
+        const long long w = y < uhi ? ((y + 1) * G - 1) / W : -1;
+        ok[k] = w >= 0;
+        sg[k] = (int)w + u;
+        if (ok[k]) y = (w + 1) * W / G;
+      }
     }
+    j0 += kMB;
     v2i ml[kMB];
     v4i o[kMB][2];
 #pragma unroll
@@ -803,9 +811,9 @@ constexpr uint32_t kAllBlocks = (1u << (4 * (D / 32))) - 1u;  // 4 query slices 
 // their number.  (Ranges that are empty when W < G take no part: their
 // blocks fall to the last arrival.)
 template <int D>
-__device__ inline uint32_t merge_share(int u, int count, long long W, int G, int gi) {
-  const long long w_first = (((long long)u * count + 1) * G - 1) / W;
-  const long long w_last = (((long long)(u + 1) * count) * G - 1) / W;
+__device__ inline uint32_t merge_share(int u, int count, long long W, int G, int ek, int gi) {
+  const long long w_first = ek > 0 ? (long long)u * ek : (((long long)u * count + 1) * G - 1) / W;
+  const long long w_last = ek > 0 ? w_first + ek - 1 : (((long long)(u + 1) * count) * G - 1) / W;
   const int nseg = (int)(w_last - w_first + 1), sidx = gi - (int)w_first;
   uint32_t m = 0u;
   for (int j = sidx; j < 4 * (D / 32); j += nseg) m |= 1u << j;
@@ -927,7 +935,25 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
   constexpr int KVB = TileLds<D>::BYTES;
   constexpr int C = TileLds<D>::COPIES;
   const long long W = (long long)U * count;
-  const long long r_lo = (long long)gi * W / G, r_hi = (long long)(gi + 1) * W / G;
+  // Range gi is pairs [gi W / G, (gi + 1) W / G) of the unit-major list.  An
+  // even split -- ek = G / U ranges per unit, each holding at least one tile
+  // -- puts range gi in unit gi / ek, as tiles [j count / ek, (j + 1) count /
+  // ek) with j = gi mod ek: the same bounds in 32-bit arithmetic.  The
+  // general case's 64-bit divisions are scalar routines of ~170 instructions
+  // each, and the merges after the loop would need 2 per segment.
+  const int ek = G % U == 0 && count >= G / U && (long long)G * count < (1ll << 31) ? G / U : 0;
+  long long r_lo, r_hi;
+  int u_first;  // unit of the range's first pair
+  if (ek > 0) {
+    u_first = gi / ek;
+    const int j = gi - u_first * ek;
+    r_lo = (long long)u_first * count + j * count / ek;
+    r_hi = (long long)u_first * count + (j + 1) * count / ek;
+  } else {
+    r_lo = (long long)gi * W / G;
+    r_hi = (long long)(gi + 1) * W / G;
+    u_first = (int)(r_lo / count);
+  }
   auto tile_of = [&](int kk) {
     if (kk >= count_r) return NTR + (kk - count_r);  // global tiles follow the ring's
     const int T = T0 + kk;
@@ -936,8 +962,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
   int fin[2], nfin = 0;  // split units with output blocks for this workgroup to merge,
   int fin_blocks[2];     // ... those blocks, with kLastArrival if it was their last arrival
 
-  for (long long x = r_lo; x < r_hi;) {
-    const int u = (int)(x / count);
+  // a segment that is not the range's last ends at its unit's end: the next
+  // one starts at tile 0 of the next unit
+  int u = u_first;
+  for (long long x = r_lo; x < r_hi; ++u) {
     const int t_lo = (int)(x - (long long)u * count);
     const long long rem = r_hi - x;
     const int t_hi = rem < count - t_lo ? t_lo + (int)rem : count;
@@ -1039,7 +1067,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
       // committed by another workgroup.
       const bool waits = x >= r_hi;
       if (threadIdx.x == 0) {
-        const uint32_t commit = waits ? merge_share<D>(u, count, W, G, gi) : 0u;
+        const uint32_t commit = waits ? merge_share<D>(u, count, W, G, ek, gi) : 0u;
         const unsigned long long old = __hip_atomic_fetch_add(
             &A.ws.sync[(size_t)u * kSyncStride], (unsigned long long)nk | ((unsigned long long)commit << 32),
             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1100,7 +1128,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
       bits &= bits - 1;
       if (n % kWaves == wave) {
         const int qs = j / DB, b = j % DB, qi = kQG * qg + 32 * qs + li;
-        merge_block<D>(pr, u, count, W, G, qs, b, lane, A.out + ((size_t)qi * H + h) * D, qi < A.n_q, ch, gq);
+        merge_block<D>(pr, u, count, W, G, ek, qs, b, lane, A.out + ((size_t)qi * H + h) * D, qi < A.n_q, ch, gq);
       }
     }
   }

@@ -213,7 +213,8 @@ def test_stress_partial_fill_sessions():
 
 @pytest.mark.parametrize("n_slots,n_heads,n_q,workgroups", [
     (3000, 6, 300, 0),      # units < workgroup slots: grid a multiple of the units
-    (3000, 6, 300, 37),     # ranges crossing unit boundaries
+    (3000, 6, 300, 37),     # 18 units: a grid of 36, two ranges per unit
+    (3000, 6, 300, 25),     # 18 units over 25 workgroups: ranges crossing unit boundaries
     (3000, 6, 300, 2048),   # more workgroups than fit on the chip at once
     (300, 2, 100, 0),       # fewer (unit, tile) pairs than workgroups: empty ranges
 ])
