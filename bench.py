@@ -13,13 +13,14 @@ Prints one JSON line.  `value` is microseconds per step (one write of 757
 tokens plus one attention call of 757 queries; the position reset, once per
 42 steps, is timed on its own and reported as `components.rotate_1layer_us`
 and its 42-step share `components.reset_share_us_per_step`).  The warm-up
-steps (600 by default, ~30 ms) bring the GPU to its sustained clock: the
-first milliseconds of work after idle run 10-15% slower.  The steps then run
-with eager launches (`components.eager_us_per_step`); the same number of
-steps is captured as one HIP graph (the device-side write position makes
-every call capturable), replayed 4 times untimed (the GPU idles while the
-graph is captured) and once timed, and `value` is the replayed time
-(`launch` says which; --no-graph reports the eager one).  Per-operation times come from separate HIP-event-timed loops
+steps (2,000 by default, ~100 ms) bring the GPU to its sustained clock: the
+first tens of milliseconds of work after idle run up to 15% slower.  The
+steps then run with eager launches (`components.eager_us_per_step`); the
+same number of steps is captured as one HIP graph (the device-side write
+position makes every call capturable), replayed 10 times untimed (the GPU
+idles for ~20 ms while the graph is captured, and takes ~7 replays to return
+to its clock) and once timed, and `value` is the replayed time (`launch`
+says which; --no-graph reports the eager one).  Per-operation times come from separate HIP-event-timed loops
 on the launch stream; `roofline` is the attention call (the dominant cost)
 against the dense FP8 matrix peak.  `cpu_baseline` times the NumPy float64
 oracle on the same work, median of 5.
@@ -52,8 +53,8 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=84)
-    ap.add_argument("--warmup", type=int, default=600,
-                    help="untimed steps first (the GPU's clock ramps up over the first ~20 ms of work)")
+    ap.add_argument("--warmup", type=int, default=2000,
+                    help="untimed steps first (the GPU's clock ramps up over the first tens of ms of work)")
     ap.add_argument("--precision", choices=["precise", "fast"], default="precise")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
@@ -336,12 +337,12 @@ def main():
     assert torch.isfinite(out.float()).all()
     ms_per_step, launch = eager_ms, "eager (one HIP launch per kernel)"
     if not args.no_graph:
-        # The same number of steps captured as one graph, replayed 4 times
+        # The same number of steps captured as one graph, replayed 10 times
         # untimed (back to the sustained clock after the capture's idle
         # time) and then once timed: exactly args.steps steps.
         first = args.warmup + args.steps
         g = capture_steps(cache, pool, pos_pool, out, first, args.steps)
-        for _ in range(4):
+        for _ in range(10):
             g.replay()
         torch.cuda.synchronize()
         a.record(stream)

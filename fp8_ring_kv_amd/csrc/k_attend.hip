@@ -27,16 +27,16 @@
 //   1. wave w loads the prepared terms of queries 32 w .. 32 w + 31;
 //   2. the tiles stream through a ring of LDS buffers: the K tile, the
 //      transposed V tile and the 128 slot scales of a tile are copied from
-//      global memory straight into LDS (global_load_lds_dwordx4) one
-//      pair of tiles ahead.  Every wave reads every tile.  Per tile a wave computes
+//      global memory straight into LDS (global_load_lds_dwordx4) two
+//      tiles ahead.  Every wave reads every tile.  Per tile a wave computes
 //      S^T = K Q^T with v_mfma_scale_f32_32x32x64_f8f6f4 (rows = slots,
 //      columns = queries: one lane owns one query, so the row max and sum
 //      are in-lane plus one swap with lane ^ 32), applies the per-slot key
 //      scale, updates an online softmax in fp32 (exp2 domain), turns
 //      P * s_v * c_h into one or two e4m3 terms and accumulates
-//      O^T += V^T P^T with the same instruction.  The two waves a SIMD holds
-//      come from different workgroups, so their matrix and vector phases
-//      overlap;
+//      O^T += V^T P^T with the same instruction.  Each wave interleaves its
+//      own matrix and vector work: the softmax of tile j runs between the
+//      P V products of tile j - 1 and the Q K^T products of tile j + 1;
 //   3. a whole unit writes its bf16 output; a unit split between
 //      workgroups writes a partial (O, max, sum) per wave, and the unit's
 //      16 output blocks are merged by the workgroups whose ranges end in it
@@ -46,7 +46,8 @@
 // Probability scale: c_h = 448 / (64 vmax_h), vmax_h being the largest value
 // scale written to head h since the reset (kept by the write kernel).  The
 // running row maximum is raised only when a tile exceeds it by more than 6
-// (log2 units), so P <= 64 and P * s_v * c_h <= 448 always fits e4m3.  (With
+// (log2 units), and then by a whole number of log2 units, so P <= 64 and
+// P * s_v * c_h <= 448 always fits e4m3.  (With
 // a headroom of 2 the raise, a wave-wide branch over 32 queries, ran on 54%
 // of the tiles of the 757 x 5,788 workload; with 6 on 14%.  The smaller c_h
 // moves only probabilities below about 1/100 of the row maximum into the
@@ -222,7 +223,7 @@ struct TileLds {
 };
 
 constexpr int kWaves = 4;          // waves per workgroup, one per SIMD
-constexpr int kBufs = 4;           // LDS ring of tile buffers: two pairs
+constexpr int kBufs = 4;           // LDS ring of tile buffers
 
 template <int D>
 __device__ inline int ksw(int r) {
@@ -292,6 +293,17 @@ __device__ inline void copy_tile(lds_u8* lbuf, const TileSrc& src, int T, const 
 template <int N>
 __device__ inline void wait_copies_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// The same with at most n tiles' copies (CW instructions each) in flight,
+// n = 0 .. 3.
+template <int CW>
+__device__ inline void wait_tiles_and_barrier(int n) {
+  switch (n) {
+    case 0: wait_copies_and_barrier<0>(); break;
+    case 1: wait_copies_and_barrier<CW>(); break;
+    case 2: wait_copies_and_barrier<2 * CW>(); break;
+    default: wait_copies_and_barrier<3 * CW>(); break;
+  }
 }
 
 // Per-wave tile operands (lane = li + 32 gq).
@@ -381,7 +393,7 @@ struct WaveState {
   v16f O[D / 32];
 };
 
-// Softmax of one tile's S^T (in registers) and its P V product.
+// Softmax of one tile's S^T (in registers), in two parts.
 // The queries carry the softmax scale log2(e)/sqrt(D), so S is in log2
 // units once multiplied by the key scale s_k.  Scores are kept relative to
 // mc = m - log2 c_h (m the running max): y - mc = fma(S, s_k, -mc), one
@@ -390,16 +402,23 @@ struct WaveState {
 // running sum l accumulates P' (so the output is O / l).  The key and value
 // scales of the 16 slots of a lane's half arrive as 16-byte LDS reads that
 // every lane of the half shares, one value per accumulator register.
+// The running max m starts at the first tile's max and moves only in whole
+// steps (log2 units): when a tile's max exceeds it by more than the headroom
+// kLazy, m rises by the ceiling of the excess, so the factor 2^(m_old -
+// m_new) that rescales O, l and the P V products of the tile before (issued
+// after the raise, with the factor in their scale operand) is an exact
+// power of two.
 // ST (the pages' static per-head scales, every valid slot of the head
 // carrying them): s_k is already in the queries, so y - mc = S - mc, and
 // l2c = log2 7, so P' = 7 P is fed as x directly (7 = 448 / 64, the
 // headroom); s_v is applied once to the output.  No per-slot scale is read.
-template <int D, int TERMS, bool ST>
-__device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>& st,
-                                  unsigned long long mask, float l2c, int lane, const lds_u8* sp) {
-  // x = P' s_v is formed once and reused; contracting x - e4m3(x) into
-  // fma(P', s_v, -e4m3(x)) would recompute the product
-#pragma clang fp contract(off)
+//
+// Part A: scores relative to mc, the mask, the tile max and the lazy raise.
+// Returns the (integer, <= 0) exponent of the rescale factor, 0 without a
+// raise.
+template <int D, bool ST>
+__device__ inline int softmax_a(v16f (&acc)[2], WaveState<D>& st, unsigned long long mask, float l2c, int lane,
+                                const lds_u8* sp) {
   constexpr int DB = D / 32;
   typedef float v4f __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) const v4f lds_v4f;
@@ -407,7 +426,6 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
   // before the first tile there is no max: scores relative to 0, and the
   // first tile always raises the max
   const float mcu = st.m == -INFINITY ? 0.f : st.m - l2c;
-  v4f sv[8];  // value scales, read while the max is found
   if constexpr (ST) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -415,17 +433,16 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
       acc[1][r] -= mcu;
     }
   } else {
-    v4f sk[8];  // all eight reads issued before the first use
 #pragma unroll
-    for (int w = 0; w < 8; ++w) sk[w] = *reinterpret_cast<lds_v4f*>(sp + 128 * (w >> 2) + 16 * (w & 3));
+    for (int sub = 0; sub < 2; ++sub) {  // the scales of a slot half, four reads issued before their use
+      v4f sk[4];
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int sub = w >> 2, r0 = 4 * (w & 3);
+      for (int w = 0; w < 4; ++w) sk[w] = *reinterpret_cast<lds_v4f*>(sp + 128 * sub + 16 * w);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[sub][r0 + e] = __builtin_fmaf(acc[sub][r0 + e], sk[w][e], -mcu);
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[sub][4 * w + e] = __builtin_fmaf(acc[sub][4 * w + e], sk[w][e], -mcu);
     }
-#pragma unroll
-    for (int w = 0; w < 8; ++w) sv[w] = *reinterpret_cast<lds_v4f*>(sp + 256 + 128 * (w >> 2) + 16 * (w & 3));
   }
   if (mask != ~0ull) {  // partially valid tile (ring edge, partial fill, padding)
     const uint32_t m0 = (uint32_t)(mask >> (16 * gq)) & 0xFFFFu;  // slots 16 gq + r
@@ -440,9 +457,15 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
 #pragma unroll
   for (int r = 1; r < 16; ++r) tmax = fmaxf(fmaxf(tmax, acc[0][r]), acc[1][r]);  // max3 chain
   tmax = half_swap_max(tmax) + mcu;  // the tile's max of y
+  int dm = 0;
   if (__ballot(tmax > st.m + kLazy) != 0ull) {
-    const float mnew = fmaxf(st.m, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
+    // The first raise sets the tile's max (there is nothing to rescale: O
+    // and l are zero); a later one moves m up by a whole number, at least
+    // to the tile's max.
+    const bool first = st.m == -INFINITY;
+    const float d = first ? -256.f : -ceilf(fmaxf(tmax - st.m, 0.f));
+    const float mnew = first ? tmax : st.m - d;
+    const float alpha = __builtin_amdgcn_exp2f(d);
     st.l *= alpha;
 #pragma unroll
     for (int b = 0; b < DB; ++b) st.O[b] *= alpha;
@@ -453,20 +476,94 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
       acc[0][r] -= shift;
       acc[1][r] -= shift;
     }
+    dm = (int)d;
   }
+  return dm;
+}
+
+// Part B: P' = exp2 of the shifted scores, the running sum, and the P terms
+// of the tile (high, and with two terms the low term 16 (x - e4m3(x))),
+// interleaved with the wave's matrix work of the iteration: the P V products
+// of the tile before (values in LDS at vb, its P terms ph0/pl0, e = their
+// rescale exponent) and the Q K^T products of the tile after (keys at kb ->
+// snext).  A wave that issues matrix instructions back to back stalls the
+// vector ALU of its SIMD while it waits for the matrix unit; between vector
+// instructions of its own, each one issues as the previous one finishes.
+// Matrix operands and value scales are read from LDS one step before their
+// use, so that few registers hold them.
+template <int D, int TERMS, bool ST, int QT>
+__device__ inline void softmax_b_mfma(v16f (&acc)[2], WaveState<D>& st, const lds_u8* sp, v8i& ph, v8i& pl,
+                                      const lds_u8* vb, const v8i& ph0, const v8i& pl0, int e, const lds_u8* kb,
+                                      const TileOffsets<D>& off, const v8i (&qf)[QT][D / 64], const int (&qs)[QT],
+                                      v16f (&snext)[2]) {
+  // x = P' s_v is formed once and reused; contracting x - e4m3(x) into
+  // fma(P', s_v, -e4m3(x)) would recompute the product
+#pragma clang fp contract(off)
+  constexpr int DB = D / 32, KS = D / 64;
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) const v4f lds_v4f;
+  // the P V products of the tile before, rescaled by 2^e through the scale
+  // operand (e >= -127: a smaller factor leaves nothing of them in fp32)
+  const int eh = 127 + (e < -127 ? -127 : e);
+  const int el = eh - 4 < 0 ? 0 : eh - 4;
+  // Matrix instruction k: first the P V products (block b, term t), then the
+  // next tile's Q K^T products (slot half sub and block ks, query term t).
+  // Operand n (of NOP) is the values of block b, then the keys of (sub, ks).
+  constexpr int NPV = DB * TERMS, NM = NPV + 2 * KS * QT;
+  constexpr int SPG = (NM + 7) / 8;  // matrix instructions per group of 4 scores
+  auto op_of = [](int k) { return k < NPV ? k / TERMS : DB + (k - NPV) / QT; };
+  auto load_op = [&](int n) {
+    if (n < DB) return lds32(vb + 2048 * n + off.v[0], vb + 2048 * n + off.v[1]);
+    const int sub = (n - DB) / KS, ks = (n - DB) % KS;
+    return lds32(kb + 32 * D * sub + off.k[ks][0], kb + 32 * D * sub + off.k[ks][1]);
+  };
+  v8i opr[2];  // operand double buffer: operand n in opr[n % 2]
+  auto mm = [&](int k) {
+    if (k >= NM) return;
+    const v8i& a = opr[op_of(k) % 2];
+    if (k < NPV) {
+      const int b = k / TERMS, t = k % TERMS;
+      st.O[b] = mfma_fp8(a, t == 0 ? ph0 : pl0, st.O[b], 127, t == 0 ? eh : el);
+    } else {
+      const int k2 = k - NPV, sub = (k2 / QT) / KS, ks = (k2 / QT) % KS, t = k2 % QT;
+      snext[sub] = mfma_fp8(a, qf[t][ks], snext[sub], 127, qs[t]);
+    }
+    // the next instruction's operand, if it needs a new one
+    if (k + 1 < NM && op_of(k + 1) != op_of(k)) opr[op_of(k + 1) % 2] = load_op(op_of(k + 1));
+  };
+  auto read_sv = [&](int w) { return *reinterpret_cast<lds_v4f*>(sp + 256 + 128 * (w >> 2) + 16 * (w & 3)); };
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) snext[sub] = v16f{};
+  opr[0] = load_op(0);
+  v4f sv[2];  // value scales of group w in sv[w % 2], read one group ahead
+  if constexpr (!ST) sv[0] = read_sv(0);
   // P' <= 64 c_h and s_v c_h <= 7, so the conversions below never
   // overflow (fp32 rounding a hair above 448 still rounds to 448 in e4m3).
-  v8i ph, pl;
+  // The vector work of each group of 4 scores comes in up to three pieces,
+  // each after one matrix instruction; scheduling barriers keep that order.
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     const int sub = w >> 2, r0 = 4 * (w & 3);
+    mm(w * SPG);
+    if constexpr (!ST) {
+      if (w + 1 < 8) sv[(w + 1) % 2] = read_sv(w + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p = __builtin_amdgcn_exp2f(acc[sub][r0 + e]);
+    for (int k = 0; k < 4; ++k) {
+      const float p = __builtin_amdgcn_exp2f(acc[sub][r0 + k]);
       st.l += p;
-      if constexpr (ST) x[e] = p;
-      else x[e] = p * sv[w][e];
+      x[k] = p;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (SPG > 1) {
+      mm(w * SPG + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (!ST) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[k] = x[k] * sv[w % 2][k];
     }
     // (the low-half conversion keeps the high half of its third operand,
     // which the high-half conversion overwrites: any value will do)
@@ -478,19 +575,21 @@ __device__ inline void softmax_pv(v16f (&acc)[2], const VOp<D>& vf, WaveState<D>
     if (TERMS == 2) {  // second term: 16 (x - e4m3(x)), descaled by 2^-4
       float d0, d1, d2, d3;
       unpack4_fp8(hw, d0, d1, d2, d3);
+      __builtin_amdgcn_sched_barrier(0);
+      if (SPG > 2) {
+        mm(w * SPG + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const float l0 = x[0] - d0;
       uint32_t lw = pack2_fp8_div<false>(l0, x[1] - d1, __float_as_uint(l0), 0.0625f);
       lw = pack2_fp8_div<true>(x[2] - d2, x[3] - d3, lw, 0.0625f);
       pl[w] = (int)lw;
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int b = 0; b < DB; ++b) {
-    st.O[b] = mfma_fp8(vf.v[b], ph, st.O[b], 127, 127);
-    if (TERMS == 2) st.O[b] = mfma_fp8(vf.v[b], pl, st.O[b], 127, 127 - 4);
-  }
+  for (int k = 8 * SPG; k < NM; ++k) mm(k);
 }
-
 
 template <int D>
 struct __attribute__((aligned(16))) AttnSmem {
@@ -823,8 +922,7 @@ __device__ inline uint32_t merge_share(int u, int count, long long W, int G, int
 // Issue priority from progress: the two waves a SIMD holds come from two
 // workgroups; the SIMD favours the older one, so without this the first
 // workgroup of every compute unit finishes well before the second, which
-// then runs alone, its matrix and vector work no longer overlapped.  A wave
-// that is behind in its segment takes precedence.
+// then runs alone.  A wave that is behind in its segment takes precedence.
 __device__ inline void set_progress_priority(int j, int nk) {
   switch ((4 * j) / nk) {
     case 0: __builtin_amdgcn_s_setprio(3); break;
@@ -835,10 +933,11 @@ __device__ inline void set_progress_priority(int j, int nk) {
 }
 
 // ---------------------------------------------------------------------------
-// Two workgroups per compute unit, 4 waves each: the two waves a SIMD holds
-// belong to different workgroups, whose barriers do not couple them, so one
-// wave's matrix instructions run while the other's softmax uses the vector
-// ALU.
+// Two workgroups of 4 waves per compute unit, one wave of each per SIMD.
+// Each wave overlaps its own matrix and vector work: while it computes the
+// softmax of tile j, its P V products of tile j - 1 and Q K^T products of
+// tile j + 1 run on the matrix unit, one instruction issued between
+// stretches of vector instructions.
 template <int D, int TERMS>
 __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
   constexpr int KS = D / 64, DB = D / 32;
@@ -1002,24 +1101,31 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
     for (int b = 0; b < DB; ++b) st.O[b] = v16f{};
     auto run_tiles = [&](auto static_tag) {
       constexpr bool ST = decltype(static_tag)::value;
-      for (int tj = 0; tj < 2 && tj < nk; ++tj)
+      // copy instructions per wave and tile (no scales with static scales)
+      constexpr int CW = ST ? TileLds<D>::COPIES - 1 : TileLds<D>::COPIES;
+      constexpr int AHEAD = kBufs - 2;  // tiles copied ahead of the one being read
+      for (int tj = 0; tj < AHEAD && tj < nk; ++tj)
         copy_tile<D, ST>(buf(tj), src, tile_of(t_lo + tj), coff, wave, lane);
-      for (int j = 0; j < nk; ++j) {
-        if ((j & 1) == 0) {
-          // a new pair of tiles: tiles j, j + 1 have landed and every wave is
-          // done with the previous pair, whose buffers take the next pair
-          wait_copies_and_barrier<0>();
-          set_progress_priority(j, nk);
-          if (j + 2 < nk) copy_tile<D, ST>(buf(j + 2), src, tile_of(t_lo + j + 2), coff, wave, lane);
-          if (j + 3 < nk) copy_tile<D, ST>(buf(j + 3), src, tile_of(t_lo + j + 3), coff, wave, lane);
-        }
-        const lds_u8* lb = buf(j);
+      // tile 0 has landed once at most the copies of tiles 1 .. AHEAD - 1 are in flight
+      wait_tiles_and_barrier<CW>(nk - 1 < AHEAD - 1 ? nk - 1 : AHEAD - 1);
+      v16f sacc[2];
+      {
         KOp<D> kf;
-        VOp<D> vf;
-        v16f sacc[2];
-        read_k<D>(kf, lb, off);
+        read_k<D>(kf, buf(0), off);
         qk<D, QT>(sacc, kf, qf, qs);
-        read_v<D>(vf, lb, off);
+      }
+      v8i ph0 = v8i{}, pl0 = v8i{};  // P terms of the tile before (none before tile 0)
+      for (int j = 0; j < nk; ++j) {
+        // Tile j + 1 (whose keys this iteration reads) has landed once at
+        // most the copies of tiles j + 2, j + 3 are in flight; after the
+        // barrier every wave is done with tile j - 2, whose buffer takes
+        // tile j + AHEAD.
+        const int last = nk - 1 < j + AHEAD - 1 ? nk - 1 : j + AHEAD - 1;  // last tile copied so far
+        const int ahead = last - (j + 1);
+        wait_tiles_and_barrier<CW>(ahead < 0 ? 0 : ahead);
+        set_progress_priority(j, nk);
+        if (j + AHEAD < nk) copy_tile<D, ST>(buf(j + AHEAD), src, tile_of(t_lo + j + AHEAD), coff, wave, lane);
+        const lds_u8* lb = buf(j);
         // Only the first and last tiles of the ring's valid range, the
         // ring's last tile (pad slots) and the last global tile can hold
         // invalid slots: the others skip the mask.
@@ -1028,12 +1134,31 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
         unsigned long long mask = ~0ull;
         if (kk == 0 || kk == count_r - 1 || kk == count - 1 || T == NTR - 1)
           mask = __ballot(slot_valid(g, T * kTile + lane, a, nv, gv));
-        softmax_pv<D, TERMS, ST>(sacc, vf, st, mask, l2c, lane, lb + off.sk4);
+        const int e = softmax_a<D, ST>(sacc, st, mask, l2c, lane, lb + off.sk4);
+        // operands of the iteration's matrix work: the keys of tile j + 1
+        // (past the last tile, tile j's again: those scores are dropped) and
+        // the values of tile j - 1 (before tile 0, tile 0's: its products
+        // with the zero P terms add nothing, and no code is a NaN)
+        v16f snext[2];
+        v8i ph, pl;
+        softmax_b_mfma<D, TERMS, ST, QT>(sacc, st, lb + off.sk4, ph, pl, buf(j > 0 ? j - 1 : 0), ph0, pl0, e,
+                                         buf(j + 1 < nk ? j + 1 : j), off, qf, qs, snext);
+        sacc[0] = snext[0];
+        sacc[1] = snext[1];
+        ph0 = ph;
+        pl0 = pl;
+      }
+      // the last tile's P V products
+      VOp<D> vf;
+      read_v<D>(vf, buf(nk - 1), off);
+#pragma unroll
+      for (int b = 0; b < DB; ++b) {
+        st.O[b] = mfma_fp8(vf.v[b], ph0, st.O[b], 127, 127);
+        if (TERMS == 2) st.O[b] = mfma_fp8(vf.v[b], pl0, st.O[b], 127, 127 - 4);
       }
     };
     if (sh) run_tiles(std::true_type{});
     else run_tiles(std::false_type{});
-
     __builtin_amdgcn_s_setprio(0);
 
     // ---- 3. whole unit: output; split unit: partial, the last to finish merges ----

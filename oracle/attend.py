@@ -41,8 +41,9 @@ The device kernel's declared numerics, which ``attend_method`` and
   every cached s_v), as hi = e4m3(x) and, with two terms, as
   lo = e4m3(16 (x - hi)) / 16; it multiplies them by the V codes and divides
   by c * sum_j P.  The kernel keeps a running row maximum that it raises only
-  when a tile exceeds it by more than 6 in log2 units, so its P may reach
-  64: headroom 6 keeps x <= 448.  ``attend_emul`` uses the final row maximum;
+  when a tile exceeds it by more than 6 in log2 units (and then by a whole
+  number of log2 units, at least up to the tile's maximum), so its P may
+  reach 64: headroom 6 keeps x <= 448.  ``attend_emul`` uses the final row maximum;
   the kernel's running maximum changes which way some codes round, which the
   tolerance covers.
 * The single-term ("fast") mode uses one term for Q and one for P.
