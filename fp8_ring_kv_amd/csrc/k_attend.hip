@@ -490,8 +490,9 @@ __device__ inline int softmax_a(v16f (&acc)[2], WaveState<D>& st, unsigned long 
 // vector ALU of its SIMD while it waits for the matrix unit; between vector
 // instructions of its own, each one issues as the previous one finishes.
 // Matrix operands and value scales are read from LDS one step before their
-// use, so that few registers hold them.
-template <int D, int TERMS, bool ST, int QT>
+// use, so that few registers hold them.  QK_ON false: no tile after (snext
+// stays zero).
+template <int D, int TERMS, bool ST, int QT, bool QK_ON = true>
 __device__ inline void softmax_b_mfma(v16f (&acc)[2], WaveState<D>& st, const lds_u8* sp, v8i& ph, v8i& pl,
                                       const lds_u8* vb, const v8i& ph0, const v8i& pl0, int e, const lds_u8* kb,
                                       const TileOffsets<D>& off, const v8i (&qf)[QT][D / 64], const int (&qs)[QT],
@@ -526,7 +527,7 @@ __device__ inline void softmax_b_mfma(v16f (&acc)[2], WaveState<D>& st, const ld
       st.O[b] = mfma_fp8(a, t == 0 ? ph0 : pl0, st.O[b], 127, t == 0 ? eh : el);
     } else {
       const int k2 = k - NPV, sub = (k2 / QT) / KS, ks = (k2 / QT) % KS, t = k2 % QT;
-      snext[sub] = mfma_fp8(a, qf[t][ks], snext[sub], 127, qs[t]);
+      if constexpr (QK_ON) snext[sub] = mfma_fp8(a, qf[t][ks], snext[sub], 127, qs[t]);
     }
     // the next instruction's operand, if it needs a new one
     if (k + 1 < NM && op_of(k + 1) != op_of(k)) opr[op_of(k + 1) % 2] = load_op(op_of(k + 1));
@@ -1115,7 +1116,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
         qk<D, QT>(sacc, kf, qf, qs);
       }
       v8i ph0 = v8i{}, pl0 = v8i{};  // P terms of the tile before (none before tile 0)
-      for (int j = 0; j < nk; ++j) {
+      // Iteration j; QK: the Q K^T products of tile j + 1 (every iteration
+      // but the last, which is peeled off the loop: a runtime test around
+      // those products, or a second copy inside the loop, spilled registers)
+      auto iter = [&](int j, auto qk_tag) {
+        constexpr bool QK = decltype(qk_tag)::value;
         // Tile j + 1 (whose keys this iteration reads) has landed once at
         // most the copies of tiles j + 2, j + 3 are in flight; after the
         // barrier every wave is done with tile j - 2, whose buffer takes
@@ -1136,18 +1141,20 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
           mask = __ballot(slot_valid(g, T * kTile + lane, a, nv, gv));
         const int e = softmax_a<D, ST>(sacc, st, mask, l2c, lane, lb + off.sk4);
         // operands of the iteration's matrix work: the keys of tile j + 1
-        // (past the last tile, tile j's again: those scores are dropped) and
-        // the values of tile j - 1 (before tile 0, tile 0's: its products
-        // with the zero P terms add nothing, and no code is a NaN)
+        // (none in the last iteration) and the values of tile j - 1 (before
+        // tile 0, tile 0's: its products with the zero P terms add nothing,
+        // and no code is a NaN)
         v16f snext[2];
         v8i ph, pl;
-        softmax_b_mfma<D, TERMS, ST, QT>(sacc, st, lb + off.sk4, ph, pl, buf(j > 0 ? j - 1 : 0), ph0, pl0, e,
-                                         buf(j + 1 < nk ? j + 1 : j), off, qf, qs, snext);
+        softmax_b_mfma<D, TERMS, ST, QT, QK>(sacc, st, lb + off.sk4, ph, pl, buf(j > 0 ? j - 1 : 0), ph0, pl0, e,
+                                             buf(QK ? j + 1 : j), off, qf, qs, snext);
         sacc[0] = snext[0];
         sacc[1] = snext[1];
         ph0 = ph;
         pl0 = pl;
-      }
+      };
+      for (int j = 0; j + 1 < nk; ++j) iter(j, std::true_type{});
+      iter(nk - 1, std::false_type{});
       // the last tile's P V products
       VOp<D> vf;
       read_v<D>(vf, buf(nk - 1), off);
