@@ -74,6 +74,17 @@ bool params_ok(const rkv_params* p, std::string* why) {
   if (p->attn_merge_wait_us < -1 || p->attn_merge_wait_us > 10000)
     return *why = "attn_merge_wait_us out of range [-1, 10000]", false;
   if (p->n_global < 0 || p->n_global > (1 << 20)) return *why = "n_global out of range [0, 2^20]", false;
+  // The attention's split partials (one per unit and per workgroup, 128
+  // queries x head_dim fp16) are addressed with 32-bit buffer offsets, and a
+  // 1 GiB offset stands for "past the end" in the merge's spare loads: the
+  // partial buffer must stay within 1 GiB (for head_dim 128 and the default
+  // grid: units = ceil(max_queries / 128) x n_heads up to 28,672).
+  {
+    const long long units = ((long long)p->max_queries + 127) / 128 * p->n_heads;
+    const long long grid = p->attn_workgroups > 0 ? p->attn_workgroups : kMaxWorkgroups;
+    if ((units + grid) * 128 * p->head_dim * 2 > (1ll << 30))
+      return *why = "ceil(max_queries / 128) x n_heads too large: the attention partials would exceed 1 GiB", false;
+  }
   const int32_t* b = p->rope_bands;
   if (b[0] || b[1] || b[2]) {
     if (b[0] < 0 || b[1] < 0 || b[2] < 0 || b[0] + b[1] + b[2] != p->head_dim / 2)

@@ -65,7 +65,11 @@ typedef struct {
   int32_t n_slots;     /* ring slots per layer N (1 .. 1<<20) */
   int32_t n_heads;     /* heads H (1 .. 256) */
   int32_t head_dim;    /* D: 64 or 128 */
-  int32_t max_queries; /* largest n_q of one cache_attend call (1 .. 1<<16) */
+  int32_t max_queries; /* largest n_q of one cache_attend call (1 .. 1<<16;
+                          also (ceil(max_queries / 128) x n_heads + the
+                          attention workgroups, 4,096 when attn_workgroups is
+                          0) x 128 x head_dim x 2 bytes of split partials
+                          <= 1 GiB) */
   int32_t precision;   /* RKV_PRECISE or RKV_FAST */
   float rope_base;     /* RoPE base, omega_j = base^(-2j/D); 10000 */
   float scale_margin;  /* scale s = margin * amax / 448; 1.0 */

@@ -143,6 +143,17 @@ def test_probes_reject_misuse_without_launching():
     assert "multiple of 16" in probe.rkv_probe_last_error()
 
 
+def test_attention_partials_stay_within_their_addressing():
+    """The split partials are addressed with 32-bit offsets and a 1 GiB
+    past-the-end offset: (units + workgroups) x 128 x head_dim x 2 bytes
+    must stay within 1 GiB."""
+    assert rkv.ring_cache_bytes(params(n_heads=256, max_queries=1 << 16)) == 0
+    assert "partials" in rkv.rkv_last_error()
+    assert rkv.ring_cache_bytes(params(n_heads=256, max_queries=1 << 16, head_dim=64)) == 0
+    assert rkv.ring_cache_bytes(params(n_heads=48, max_queries=1 << 16)) > 0  # 24,576 units + 4,096
+    assert rkv.ring_cache_bytes(params(n_heads=256, max_queries=14336)) > 0  # 28,672 units + 4,096
+
+
 def test_rope_band_and_global_parameters_are_checked():
     assert rkv.ring_cache_bytes(params(rope_bands=(22, 21, 21), n_global=1246)) > 0
     assert rkv.ring_cache_bytes(params(rope_bands=(22, 21, 20))) == 0  # 63 pairs, not 64
