@@ -1087,14 +1087,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void attend_kernel(AttnArgs A) {
     auto buf = [&](int tj) { return kv0 + (tj % kBufs) * KVB; };
 
     // ---- 1. the unit's queries (unless already loaded), then the copies of
-    //         the first pair of tiles ----
+    //         the first two tiles ----
     const int qi = kQG * qg + 32 * wave + li;
     if (u != u_pre) load_q(u);
 
-    // ---- 2. the segment's tiles, in pairs.  Tile t sits in buffer t % 4.
-    //         One barrier per pair: after it, the pair's tiles have landed and
-    //         the previous pair's buffers are free for the next pair's copies,
-    //         which then have one pair of compute to land ----
+    // ---- 2. the segment's tiles, copied two ahead into the ring of 4
+    //         buffers (tile t in buffer t % 4), one barrier per tile.
+    //         Iteration j computes the softmax of tile j between the P V
+    //         products of tile j - 1 and the Q K^T products of tile j + 1 ----
     WaveState<D> st;
     st.m = -INFINITY;
     st.l = 0.f;
