@@ -32,7 +32,8 @@ import fp8_ring_kv_amd as rkv
 from oracle import attend as oatt, ring as oring
 from oracle.bf16 import round_bf16
 from tests.gpu_common import DEV, attn_errors, check_attention, gate, pos_dev, require_gpu, to_dev
-from workloads import ATTEND, STRESS, TINY, Bf16, Config, OutlierSpec, Stream, positions
+from workloads import (ATTEND, STRESS, TINY, Bf16, Config, OutlierSpec, Stream, bf16_bits_to_f64, f32_to_bf16_bits,
+                       positions)
 
 pytestmark = pytest.mark.gpu
 
@@ -246,6 +247,44 @@ def test_merge_schedule_leaves_results_unchanged(n_slots, n_heads, n_q, workgrou
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     check_attention(f"merge schedule ({workgroups} workgroups)", caches[0], 0, st, q.f64, qpos, gpu_out(outs[0]))
+
+
+@pytest.mark.parametrize("alpha", [8.0, 40.0])
+def test_running_max_jumps_mid_segment(alpha):
+    """A block of keys alpha times larger than the rest, in the middle of
+    every workgroup range that meets it (16 workgroups: ~12-tile ranges), so
+    that the running maximum rises by tens of log2 units (alpha 8) or by
+    more than the 127 that the E8M0 operand can carry (alpha 40) between two
+    tiles of one segment: the delayed P.V products of the tile before the
+    raise take the rescale through their scale operand, clamped at 2^-127
+    where nothing of them would survive in fp32 anyway.  Precise mode,
+    checked against exact attention."""
+    n_slots, n_heads, n_q = 3000, 2, 200
+    rng = np.random.default_rng(77)
+    cache = rkv.RingCache(1, n_slots, n_heads, 128, n_q, device=DEV, attn_workgroups=16)
+    st = oring.RingState(n_slots, n_heads, 128)
+
+    def bf16(x):
+        bits = f32_to_bf16_bits(x)
+        return Bf16(bits=bits, f64=bf16_bits_to_f64(bits))
+
+    p0 = 0
+    for c in range(2):
+        n = 1500
+        k = rng.standard_normal((n, n_heads, 128), dtype=np.float32)
+        v = rng.standard_normal((n, n_heads, 128), dtype=np.float32)
+        if c == 0:
+            k[1400:1500] *= np.float32(alpha)  # slots 1,400 .. 1,499: tiles 21 .. 23
+        kb, vb = bf16(k), bf16(v)
+        pos = positions(p0, n)
+        cache.write(0, to_dev(kb), to_dev(vb), pos_dev(pos))
+        oring.write(st, kb.f64, vb.f64, pos)
+        p0 += n
+    qb = bf16(rng.standard_normal((n_q, n_heads, 128), dtype=np.float32))
+    qpos = positions(p0, n_q)
+    out = gpu_out(cache.attend(0, to_dev(qb), pos_dev(qpos)))
+    assert np.isfinite(out).all()
+    check_attention(f"max jump x{alpha:g}", cache, 0, st, qb.f64, qpos, out)
 
 
 def test_attend_rejects_bad_arguments():
