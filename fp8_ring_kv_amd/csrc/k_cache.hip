@@ -144,8 +144,9 @@ __global__ __launch_bounds__(256) void calibrate_kernel(Geom g, int layer_lo, fl
   // is bf16 until the calibration and FP8 with the head's scales from then
   // on): code' = e4m3(code * s_slot / s) with the product and quotient in
   // double precision, so that every valid slot carries the head's scales
-  // and the attention can apply them per head.  Nothing saturates: every
-  // element is at most amax <= 448 s / margin.  Only this workgroup touches
+  // and the attention can apply them per head.  Every element is at most
+  // amax = 448 s / margin, so only a margin below 1 saturates (at +-448,
+  // the clamp below).  Only this workgroup touches
   // the head's slots, and every one of its reads above came before the
   // reduction's barriers.
   auto requant16 = [](uint4 w, const float* sc, bool per_elem, float s) {

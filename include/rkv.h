@@ -54,7 +54,7 @@ enum {
 
 /* Attention precision (the config switch keeps the plain path, §8 "Keep the
  * plain path behind every switch").
- *   RKV_PRECISE: Q enters the FP8 products as two power-of-two-scaled e4m3
+ *   RKV_PRECISE: Q enters the FP8 products as three power-of-two-scaled e4m3
  *                terms and the probabilities as two e4m3 terms (hi + lo/16).
  *   RKV_FAST:    one term each (plain FP8 attention as in §4.3). */
 enum { RKV_PRECISE = 0, RKV_FAST = 1 };
@@ -271,16 +271,20 @@ int ring_cache_set_qk_norm(rkv_cache* c, int32_t layer, const void* wq_bf16, con
  * first steps filled, times a margin; values beyond them saturate; a reset
  * rotation keeps them and clamps).  For each layer (-1: all) this enqueues a
  * kernel that takes, per head, the largest magnitude of the dequantized keys
- * and of the values over the valid slots and sets the static scales
- * s = fp32(margin * amax / 448) (amax and the product in double precision).
+ * and of the values over the valid slots, sets the static scales
+ * s = fp32(margin * amax / 448) (amax and the product in double precision)
+ * and requantizes the head's valid keys and values to them
+ * (code' = e4m3(code * s_slot / s), product and quotient in double
+ * precision, saturating at +-448, which only a margin below 1 reaches).
  * From then on, every write of the layer quantizes with these scales
  * (e4m3 of the correctly rounded y / s, saturating) and stores them as the
- * slots' scales, and every delta rotation requantizes each valid key with
- * its head's static key scale and clamps (keys written before the
- * calibration move from their per-token scale to the head's).  A head whose
- * amax is 0 (nothing valid, or all zero) gets scale 0 and keeps the
- * per-(token, head) rule for its keys (values).  The attention reads the
- * slots' scales as before.  ring_cache_reset returns the layer to
+ * slots' scales, every delta rotation requantizes each valid key with its
+ * head's static key scale and clamps, and the attention applies the head's
+ * two scales once (the key scale folded into the queries, the value scale
+ * on the output) instead of reading per-slot scales.  A head whose amax is
+ * 0 (nothing valid, or all zero) gets scale 0 and keeps the per-(token,
+ * head) rule for its keys (values); a head with either scale 0 is attended
+ * with its per-slot scales.  ring_cache_reset returns the layer to
  * per-(token, head) scales.  The mode is device state (graph-capturable).
  * margin in (0, 64] (the pages use 1.5).  Errors: RKV_EINVAL for a null
  * cache, a layer out of range or a bad margin; RKV_EHIP if the launch fails. */

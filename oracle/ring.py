@@ -273,7 +273,8 @@ def calibrate_static(st: RingState, margin: float) -> None:
     # scales from then on; this cache is FP8 from the first write, so the
     # calibration requantizes every valid key and value of a calibrated head
     # with the head's scale (one more e4m3 rounding of the per-token codes;
-    # nothing saturates: every element is at most amax <= 448 s / margin).
+    # every element is at most amax = 448 s / margin, so only a margin below
+    # 1 saturates, at +-448 as encode does).
     # Every valid slot then carries its head's scales, which is what lets the
     # attention apply them per head.
     for h in range(st.n_heads):

@@ -70,6 +70,40 @@ def test_static_session_matches_oracle():
     check_attention("static session", cache, 0, st, q.f64, qpos, out)
 
 
+def test_margin_below_one_saturates_like_the_oracle():
+    """A margin below 1 puts the head's largest elements beyond 448 s: the
+    calibration's requantization and every later static write clamp them at
+    +-448 (code 0x7E / 0xFE), on the device as in the oracle; the attention
+    over the clamped cache against exact fp64 attention on the same cache."""
+    cfg = Config("static_sat", n_heads=2, head_dim=128, n_slots=500, chunk=200, seed=37,
+                 outliers=OutlierSpec(0.02, 8.0))
+    cache = rkv.RingCache(1, cfg.n_slots, 2, 128, 200, rkv.RKV_PRECISE, device=DEV)
+    st = oring.RingState(cfg.n_slots, 2, 128)
+    s = Stream(cfg)
+    for c in range(2):
+        _, k, v = s.chunk()
+        pos = positions(200 * c, 200)
+        cache.write(0, to_dev(k), to_dev(v), pos_dev(pos))
+        oring.write(st, k.f64, v.f64, pos)
+    cache.calibrate_static(0, 0.75)
+    oring.calibrate_static(st, 0.75)
+    got = cache.static_scales(0).cpu().numpy().astype(np.float64)
+    assert np.array_equal(got[1], st.static_v), (got[1], st.static_v)
+    assert np.all(np.abs(got[0] - st.static_k) <= st.static_k * 2.0 ** -22), (got[0] - st.static_k, st.static_k)
+    st.static_k = got[0].copy()
+    assert_cache_matches(cache, 0, st)
+    kc, vc = (t.cpu().numpy() for t in cache.codes(0))
+    for name, codes in (("keys", kc), ("values", vc)):  # the clamp was reached
+        assert np.any((codes & 0x7F) == 0x7E), f"no saturated {name} after calibrating at 0.75"
+    q, k, v = s.chunk()
+    pos = positions(400, 200)
+    cache.write(0, to_dev(k), to_dev(v), pos_dev(pos))  # static write, saturating
+    oring.write(st, k.f64, v.f64, pos)
+    assert_cache_matches(cache, 0, st)
+    out = cache.attend(0, to_dev(q), pos_dev(pos)).float().cpu().numpy().astype(np.float64)
+    check_attention("static scales at margin 0.75", cache, 0, st, q.f64, pos, out)
+
+
 def test_rotation_right_after_calibration():
     """Keys written with per-token scales, calibrated, then rotated before any
     rewrite: the rotation moves them to the head's static scale, which covers
