@@ -1,4 +1,4 @@
-// FP8 attention over the ring cache for gfx950, one launch per call.
+// FP8 attention over the ring cache for gfx950.
 //
 // Runway Characters paper: every call attends its new queries over all
 // slots of its cache, after the chunk was written (§2 "The step budget",
